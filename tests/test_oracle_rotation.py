@@ -1,0 +1,71 @@
+"""Pins for oracle/rpbh.py (RPBH rotation as a dense matrix).
+
+RPBH definition: OrbitQuant summary (picx.dev), "Randomized Permuted
+Block-Hadamard (RPBH) Rotation"; orthogonality: "Offline Weight Quantization";
+cancellation: "Online Activation Quantization".
+"""
+import numpy as np
+import pytest
+import scipy.linalg
+
+import oracle
+import workloads
+
+
+@pytest.mark.parametrize("h", [1, 2, 4, 8, 16, 32, 64, 128, 256])
+def test_hadamard_is_sylvester_and_orthogonal(h):
+    H = oracle.hadamard(h)
+    # scipy builds the Sylvester matrix by recursive doubling, a different construction
+    assert np.array_equal(H, scipy.linalg.hadamard(h))
+    assert np.array_equal(H @ H.T, h * np.eye(h, dtype=np.int64))
+
+
+@pytest.mark.parametrize("d,h", [(256, 64), (384, 128), (512, 128), (192, 64)])
+def test_rpbh_orthogonal_and_norm_preserving(d, h):
+    perm, signs = workloads.rotation(d, seed=7 + d)
+    Pi = oracle.rpbh_matrix(d, h, perm, signs)
+    assert np.max(np.abs(Pi @ Pi.T - np.eye(d))) < 1e-12
+    x = np.random.default_rng(1).standard_normal((5, d))
+    xr = oracle.rotate(x, Pi)
+    assert np.allclose(np.linalg.norm(xr, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+
+
+def test_rpbh_identity_permutation_is_block_hadamard():
+    d, h = 256, 64
+    Pi = oracle.rpbh_matrix(d, h, np.arange(d), np.ones(d, np.int8))
+    ref = scipy.linalg.block_diag(*([scipy.linalg.hadamard(h) / np.sqrt(h)] * (d // h)))
+    assert np.array_equal(Pi, ref)
+
+
+@pytest.mark.parametrize("d,h", [(256, 64), (384, 128)])
+def test_rpbh_factor_order_and_conventions(d, h):
+    """x' = blkdiag(H_h D_i) P_pi x with (P x)_j = x[perm[j]] and D applied after P,
+    built here from scipy's Hadamard block by block instead of one dense matrix."""
+    perm, signs = workloads.rotation(d, seed=3 * d)
+    x = np.random.default_rng(2).standard_normal(d)
+    y = x[perm] * signs                      # D P x
+    Hs = scipy.linalg.hadamard(h) / np.sqrt(h)
+    ref = np.concatenate([Hs @ y[b * h:(b + 1) * h] for b in range(d // h)])
+    got = oracle.rotate(x[None, :], oracle.rpbh_matrix(d, h, perm, signs))[0]
+    assert np.allclose(got, ref, rtol=0, atol=1e-13)
+    # the reversed order (sign by original index) must give a different result
+    wrong = np.concatenate([Hs @ (x * signs)[perm][b * h:(b + 1) * h] for b in range(d // h)])
+    assert not np.allclose(got, wrong)
+
+
+def test_rotation_cancels_in_unquantized_product():
+    """(X Pi^T)(W Pi^T)^T = X W^T (spec bound 1e-5 relative; float64 gives ~1e-15)."""
+    d, h = 384, 128
+    perm, signs = workloads.rotation(d)
+    Pi = oracle.rpbh_matrix(d, h, perm, signs)
+    rng = np.random.default_rng(5)
+    X = rng.standard_t(3, (40, d)) * np.exp(rng.standard_normal(d))
+    W = rng.standard_normal((30, d)) * 0.02
+    Y = oracle.unquantized_fold(X, W, Pi)
+    ref = X @ W.T
+    assert np.linalg.norm(Y - ref) / np.linalg.norm(ref) < 1e-12
+
+
+def test_rpbh_rejects_non_permutation():
+    with pytest.raises(ValueError):
+        oracle.rpbh_matrix(128, 64, np.zeros(128, np.int64), np.ones(128))
