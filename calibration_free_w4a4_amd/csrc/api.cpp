@@ -1,0 +1,275 @@
+// C ABI of liborbq (declared and documented in include/orbq.h): argument checks on the host,
+// then asynchronous launches of the rpbh_quantize and lut_gemm kernels.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "../../include/orbq.h"
+#include "internal.h"
+
+#define ORBQ_API extern "C" __attribute__((visibility("default")))
+
+namespace {
+
+thread_local char g_last_error[512] = "";
+
+int fail(int status, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+int fail(int status, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_last_error, sizeof(g_last_error), fmt, ap);
+  va_end(ap);
+  return status;
+}
+
+int ok() {
+  g_last_error[0] = '\0';
+  return ORBQ_OK;
+}
+
+bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+bool supported_bits(int b) { return b == 2 || b == 4 || b == 6; }
+
+int check_codebook(const orbq_codebook* cb, int64_t d, const char* what) {
+  if (!cb) return fail(ORBQ_ERR_INVALID_ARG, "%s: codebook is NULL", what);
+  if (!cb->centroids) return fail(ORBQ_ERR_INVALID_ARG, "%s: codebook centroids are NULL", what);
+  if (!supported_bits(cb->bits)) return fail(ORBQ_ERR_UNSUPPORTED, "%s: codebook bits %d not in {2,4,6}", what, cb->bits);
+  if (d >= 0 && cb->d != d) return fail(ORBQ_ERR_INVALID_ARG, "%s: codebook d=%d but d=%lld", what, cb->d, (long long)d);
+  const int n = 1 << cb->bits;
+  for (int k = 0; k < n; ++k) {
+    if (!std::isfinite(cb->centroids[k])) return fail(ORBQ_ERR_CODEBOOK, "%s: centroid %d not finite", what, k);
+    if (k && !(cb->centroids[k] > cb->centroids[k - 1]))
+      return fail(ORBQ_ERR_CODEBOOK, "%s: centroids not strictly ascending at %d", what, k);
+    if (cb->centroids[n - 1 - k] != -cb->centroids[k])
+      return fail(ORBQ_ERR_CODEBOOK, "%s: centroids not antisymmetric at %d", what, k);
+  }
+  return ORBQ_OK;
+}
+
+int check_rot(const orbq_rpbh* rot, int64_t d, const char* what) {
+  if (!rot) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation is NULL", what);
+  if (!rot->perm || !rot->signs) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation arrays are NULL", what);
+  if (rot->d != d) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation d=%d but d=%lld", what, rot->d, (long long)d);
+  if (rot->block != 64 && rot->block != 128)
+    return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not in {64,128}", what, rot->block);
+  if (d % rot->block) return fail(ORBQ_ERR_INVALID_ARG, "%s: d=%lld not a multiple of block %d", what, (long long)d, rot->block);
+  return ORBQ_OK;
+}
+
+int check_dim(int64_t d, const char* what) {
+  if (d <= 0) return fail(ORBQ_ERR_INVALID_ARG, "%s: d=%lld must be positive", what, (long long)d);
+  if (d > 16384) return fail(ORBQ_ERR_UNSUPPORTED, "%s: d=%lld above 16384", what, (long long)d);
+  return ORBQ_OK;
+}
+
+int quant_params(const orbq_codebook* cb, orbq::QuantParams* qp, const char* what) {
+  if (orbq::build_quant_params(cb->centroids, cb->bits, qp))
+    return fail(ORBQ_ERR_CODEBOOK, "%s: no power-of-two scale separates the decision thresholds", what);
+  return ORBQ_OK;
+}
+
+int hip_status(int e, const char* what) {
+  if (e != hipSuccess) return fail(ORBQ_ERR_HIP, "%s: %s", what, hipGetErrorString(static_cast<hipError_t>(e)));
+  return ok();
+}
+
+// shared by orbq_rpbh_quantize and orbq_fold_weights
+int quantize_rows(orbq::QuantMode mode, const void* X, int64_t n, int64_t d, int64_t ld, const orbq_rpbh* rot,
+                  const orbq_codebook* cb, float eps, uint8_t* codes, void* norms, size_t norm_align,
+                  void* stream, const char* what) {
+  int s;
+  if ((s = check_dim(d, what))) return s;
+  if (n < 0) return fail(ORBQ_ERR_INVALID_ARG, "%s: n=%lld negative", what, (long long)n);
+  if (ld < d) return fail(ORBQ_ERR_INVALID_ARG, "%s: ld=%lld < d=%lld", what, (long long)ld, (long long)d);
+  if ((s = check_rot(rot, d, what))) return s;
+  if ((s = check_codebook(cb, d, what))) return s;
+  if (!(eps >= 0.0f) || !std::isfinite(eps)) return fail(ORBQ_ERR_INVALID_ARG, "%s: eps must be finite and >= 0", what);
+  if (n == 0) return ok();
+  if (!X || !codes || !norms) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL buffer", what);
+  if (!aligned(X, 16) || (ld * 2) % 16) return fail(ORBQ_ERR_ALIGNMENT, "%s: input must be 16-byte aligned with a 16-byte pitch", what);
+  if (!aligned(codes, 16)) return fail(ORBQ_ERR_ALIGNMENT, "%s: codes must be 16-byte aligned", what);
+  if (!aligned(norms, norm_align)) return fail(ORBQ_ERR_ALIGNMENT, "%s: norms misaligned", what);
+  orbq::QuantParams qp;
+  if ((s = quant_params(cb, &qp, what))) return s;
+  orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs};
+  const int e = orbq::launch_rpbh_quantize(mode, static_cast<const uint16_t*>(X), n, ld, ra, &qp, eps, codes, norms,
+                                           nullptr, static_cast<hipStream_t>(stream));
+  return hip_status(e, what);
+}
+
+}  // namespace
+
+ORBQ_API int orbq_codebook_lloyd_max(int32_t d, int32_t bits, float* centroids_out) {
+  if (!centroids_out) return fail(ORBQ_ERR_INVALID_ARG, "orbq_codebook_lloyd_max: output is NULL");
+  if (d < 3 || bits < 1 || bits > 8) return fail(ORBQ_ERR_INVALID_ARG, "orbq_codebook_lloyd_max: need d >= 3, 1 <= bits <= 8");
+  std::vector<double> c(1u << bits);
+  if (orbq::lloyd_max_host(d, bits, c.data())) return fail(ORBQ_ERR_INVALID_ARG, "orbq_codebook_lloyd_max: no convergence");
+  for (size_t k = 0; k < c.size(); ++k) centroids_out[k] = static_cast<float>(c[k]);
+  return ok();
+}
+
+ORBQ_API int orbq_rpbh_validate(int32_t d, int32_t block, const int32_t* perm, const int8_t* signs) {
+  const char* what = "orbq_rpbh_validate";
+  if (!perm || !signs) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL array", what);
+  int s;
+  if ((s = check_dim(d, what))) return s;
+  if (block != 64 && block != 128) return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not in {64,128}", what, block);
+  if (d % block) return fail(ORBQ_ERR_INVALID_ARG, "%s: d not a multiple of block", what);
+  std::vector<unsigned char> seen(d, 0);
+  for (int j = 0; j < d; ++j) {
+    if (perm[j] < 0 || perm[j] >= d || seen[perm[j]]) return fail(ORBQ_ERR_INVALID_ARG, "%s: perm is not a permutation (entry %d)", what, j);
+    seen[perm[j]] = 1;
+    if (signs[j] != 1 && signs[j] != -1) return fail(ORBQ_ERR_INVALID_ARG, "%s: sign %d is not +-1", what, j);
+  }
+  return ok();
+}
+
+ORBQ_API int orbq_codebook_validate(const orbq_codebook* cb) {
+  int s = check_codebook(cb, -1, "orbq_codebook_validate");
+  if (s) return s;
+  orbq::QuantParams qp;
+  if ((s = quant_params(cb, &qp, "orbq_codebook_validate"))) return s;
+  return ok();
+}
+
+ORBQ_API size_t orbq_codes_row_bytes(int64_t d, int32_t bits) {
+  if (d <= 0 || bits <= 0 || (d * bits) % 8) return 0;
+  return static_cast<size_t>(d * bits / 8);
+}
+
+ORBQ_API int orbq_fold_weights(const void* W, int64_t m, int64_t d, int64_t ldw, const orbq_rpbh* rot,
+                               const orbq_codebook* cb_w, float eps, uint8_t* w_codes, void* w_norms, void* stream) {
+  return quantize_rows(orbq::QuantMode::kWeights, W, m, d, ldw, rot, cb_w, eps, w_codes, w_norms, 2, stream,
+                       "orbq_fold_weights");
+}
+
+ORBQ_API int orbq_rpbh_quantize(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                                const orbq_codebook* cb_a, float eps, uint8_t* x_codes, float* x_norms, void* stream) {
+  return quantize_rows(orbq::QuantMode::kActivations, X, n, d, ldx, rot, cb_a, eps, x_codes, x_norms, 4, stream,
+                       "orbq_rpbh_quantize");
+}
+
+namespace {
+
+int gemm_checks(const uint8_t* x_codes, const float* x_norms, const orbq_codebook* cb_a, const uint8_t* w_codes,
+                const void* w_norms, const orbq_codebook* cb_w, int64_t n, int64_t m, int64_t d, void* Y,
+                orbq_dtype y_type, int64_t ldy, const char* what, bool check_x) {
+  int s;
+  if ((s = check_dim(d, what))) return s;
+  if (d % 64) return fail(ORBQ_ERR_UNSUPPORTED, "%s: d=%lld not a multiple of 64", what, (long long)d);
+  if (n < 0 || m < 0) return fail(ORBQ_ERR_INVALID_ARG, "%s: negative n or m", what);
+  if (ldy < m) return fail(ORBQ_ERR_INVALID_ARG, "%s: ldy=%lld < m=%lld", what, (long long)ldy, (long long)m);
+  if (y_type != ORBQ_F32 && y_type != ORBQ_BF16) return fail(ORBQ_ERR_INVALID_ARG, "%s: bad y_type", what);
+  if ((s = check_codebook(cb_a, d, what))) return s;
+  if ((s = check_codebook(cb_w, d, what))) return s;
+  if (n == 0 || m == 0) return ORBQ_OK;
+  if ((check_x && (!x_codes || !x_norms)) || !w_codes || !w_norms || !Y)
+    return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL buffer", what);
+  if ((check_x && (!aligned(x_codes, 16) || !aligned(x_norms, 4))) || !aligned(w_codes, 16) || !aligned(w_norms, 2))
+    return fail(ORBQ_ERR_ALIGNMENT, "%s: codes must be 16-byte aligned, norms naturally aligned", what);
+  const int64_t esz = y_type == ORBQ_F32 ? 4 : 2;
+  if (!aligned(Y, 16) || (ldy * esz) % 16) return fail(ORBQ_ERR_ALIGNMENT, "%s: Y must be 16-byte aligned with a 16-byte pitch", what);
+  return ORBQ_OK;
+}
+
+int gemm_launch(const uint8_t* x_codes, const float* x_norms, const orbq_codebook* cb_a, const uint8_t* w_codes,
+                const void* w_norms, const orbq_codebook* cb_w, int64_t n, int64_t m, int64_t d, void* Y,
+                orbq_dtype y_type, int64_t ldy, void* stream, const char* what) {
+  orbq::DecodeParams da, dw;
+  orbq::build_decode_params(cb_a->centroids, cb_a->bits, &da);
+  orbq::build_decode_params(cb_w->centroids, cb_w->bits, &dw);
+  const int e = orbq::launch_lut_gemm(x_codes, x_norms, da, w_codes, static_cast<const uint16_t*>(w_norms), dw, n, m, d,
+                                      Y, y_type == ORBQ_BF16, ldy, static_cast<hipStream_t>(stream));
+  return hip_status(e, what);
+}
+
+size_t ws_codes_bytes(int64_t n, int64_t d, int32_t bits) {
+  return (static_cast<size_t>(n) * static_cast<size_t>(d * bits / 8) + 255) & ~size_t(255);
+}
+
+}  // namespace
+
+ORBQ_API int orbq_lut_gemm(const uint8_t* x_codes, const float* x_norms, const orbq_codebook* cb_a,
+                           const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w, int64_t n, int64_t m,
+                           int64_t d, void* Y, orbq_dtype y_type, int64_t ldy, void* stream) {
+  const char* what = "orbq_lut_gemm";
+  int s = gemm_checks(x_codes, x_norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, what, true);
+  if (s) return s;
+  if (n == 0 || m == 0) return ok();
+  return gemm_launch(x_codes, x_norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, stream, what);
+}
+
+ORBQ_API size_t orbq_linear_workspace_bytes(int64_t n, int64_t d, int32_t bits_a) {
+  if (n < 0 || d <= 0 || !supported_bits(bits_a)) return 0;
+  return ws_codes_bytes(n, d, bits_a) + static_cast<size_t>(n) * sizeof(float);
+}
+
+ORBQ_API int orbq_linear(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                         const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
+                         const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes, void* Y,
+                         orbq_dtype y_type, int64_t ldy, void* stream) {
+  const char* what = "orbq_linear";
+  int s = gemm_checks(nullptr, nullptr, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, what, false);
+  if (s) return s;
+  if ((s = check_rot(rot, d, what))) return s;
+  if (ldx < d) return fail(ORBQ_ERR_INVALID_ARG, "%s: ldx < d", what);
+  if (n == 0 || m == 0) return ok();
+  const size_t need = orbq_linear_workspace_bytes(n, d, cb_a->bits);
+  if (!workspace || ws_bytes < need)
+    return fail(ORBQ_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what, ws_bytes, need);
+  if (!aligned(workspace, 256)) return fail(ORBQ_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", what);
+  uint8_t* codes = static_cast<uint8_t*>(workspace);
+  float* norms = reinterpret_cast<float*>(codes + ws_codes_bytes(n, d, cb_a->bits));
+  s = quantize_rows(orbq::QuantMode::kActivations, X, n, d, ldx, rot, cb_a, eps, codes, norms, 4, stream, what);
+  if (s) return s;
+  return gemm_launch(codes, norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, stream, what);
+}
+
+ORBQ_API const char* orbq_status_string(int status) {
+  switch (status) {
+    case ORBQ_OK: return "ORBQ_OK";
+    case ORBQ_ERR_INVALID_ARG: return "ORBQ_ERR_INVALID_ARG";
+    case ORBQ_ERR_UNSUPPORTED: return "ORBQ_ERR_UNSUPPORTED";
+    case ORBQ_ERR_ALIGNMENT: return "ORBQ_ERR_ALIGNMENT";
+    case ORBQ_ERR_WORKSPACE: return "ORBQ_ERR_WORKSPACE";
+    case ORBQ_ERR_HIP: return "ORBQ_ERR_HIP";
+    case ORBQ_ERR_CODEBOOK: return "ORBQ_ERR_CODEBOOK";
+    default: return "ORBQ_ERR_UNKNOWN";
+  }
+}
+
+ORBQ_API const char* orbq_last_error(void) { return g_last_error; }
+
+ORBQ_API int orbq_test_rotate(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot, float* x_rot,
+                              float* x_norms, void* stream) {
+  const char* what = "orbq_test_rotate";
+  int s;
+  if ((s = check_dim(d, what))) return s;
+  if ((s = check_rot(rot, d, what))) return s;
+  if (n < 0 || ldx < d) return fail(ORBQ_ERR_INVALID_ARG, "%s: bad n or ldx", what);
+  if (n == 0) return ok();
+  if (!X || !x_rot || !x_norms) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL buffer", what);
+  if (!aligned(X, 16) || (ldx * 2) % 16 || !aligned(x_rot, 16))
+    return fail(ORBQ_ERR_ALIGNMENT, "%s: misaligned buffer", what);
+  orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs};
+  const int e = orbq::launch_rpbh_quantize(orbq::QuantMode::kRotateOnly, static_cast<const uint16_t*>(X), n, ldx, ra,
+                                           nullptr, 0.0f, nullptr, x_norms, x_rot, static_cast<hipStream_t>(stream));
+  return hip_status(e, what);
+}
+
+ORBQ_API int orbq_test_quantize_t(const float* t, int64_t count, const orbq_codebook* cb, uint8_t* codes, void* stream) {
+  const char* what = "orbq_test_quantize_t";
+  int s = check_codebook(cb, -1, what);
+  if (s) return s;
+  if (count < 0) return fail(ORBQ_ERR_INVALID_ARG, "%s: negative count", what);
+  if (count == 0) return ok();
+  if (!t || !codes) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL buffer", what);
+  orbq::QuantParams qp;
+  if ((s = quant_params(cb, &qp, what))) return s;
+  return hip_status(orbq::launch_quantize_t(t, count, qp, codes, static_cast<hipStream_t>(stream)), what);
+}

@@ -1,0 +1,70 @@
+// Internal declarations shared by the host layer and the kernels of liborbq.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace orbq {
+
+constexpr int kMaxPosBoundaries = 31;  // 6-bit codebooks: N/2 - 1 positive decision boundaries
+constexpr int kMaxTableHalf = 256;     // quantizer table holds buckets -J..J-1, J <= 256
+
+// Decision thresholds of one codebook in the scaled coordinate t' = t * 2^k.
+//
+// Positive centroids c_{N/2+p} (p = 0..N/2-1) are separated by the exact midpoints
+// B_p = (c_{N/2+p} + c_{N/2+p+1}) / 2.  For fp32 t':
+//   t' > 0 : rank = #{p : t' > B_p}            (ties -> lower index -> lower rank)
+//   t' <= 0: rank = #{p : |t'| >= B_p}         (ties -> lower index -> higher rank)
+// thr_gt[p] = largest float <= B_p * 2^k, so  t' > B_p  <=>  t' > thr_gt[p];
+// thr_ge[p] = largest float <  B_p * 2^k, so  u >= B_p  <=>  u > thr_ge[p].
+// 2^k is chosen so that neighbouring thresholds are at least 1.5 apart: every unit
+// bucket of t' then holds at most one threshold, which lets the kernels decide with one
+// table lookup and one compare per coordinate.
+struct QuantParams {
+  float scale;  // 2^k
+  int32_t J;    // buckets j = floor(-t') are clamped to [-J, J-1]
+  int32_t nb;   // number of positive boundaries, N/2 - 1
+  int32_t bits;
+  float thr_gt[kMaxPosBoundaries + 1];
+  float thr_ge[kMaxPosBoundaries + 1];
+};
+
+// Host: builds QuantParams from an ascending, antisymmetric fp32 codebook.
+// Returns 0 on success, nonzero when no power-of-two scale separates the thresholds.
+int build_quant_params(const float* centroids, int bits, QuantParams* qp);
+
+// Host: float64 Lloyd-Max for f_d (codebook.cpp).
+int lloyd_max_host(int d, int bits, double* out);
+
+// Decode tables for the product: bf16 bit patterns of the centroid magnitudes, by rank.
+struct DecodeParams {
+  int32_t bits;
+  uint16_t mag[32];  // bf16(|c_{N/2+r}|), r = 0..N/2-1
+};
+void build_decode_params(const float* centroids, int bits, DecodeParams* dp);
+
+uint16_t f32_to_bf16_rne(float x);
+
+// Launchers (return hipError_t as int).
+struct RotArgs {
+  int32_t d, block;
+  const int32_t* perm;
+  const int8_t* signs;
+};
+
+enum class QuantMode { kActivations, kWeights, kRotateOnly };
+
+int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t ldx, const RotArgs& rot,
+                         const QuantParams* qp, float eps, uint8_t* codes, void* norms, float* x_rot,
+                         hipStream_t stream);
+
+int launch_quantize_t(const float* t, int64_t count, const QuantParams& qp, uint8_t* codes,
+                      hipStream_t stream);
+
+int launch_lut_gemm(const uint8_t* x_codes, const float* x_norms, const DecodeParams& da,
+                    const uint8_t* w_codes, const uint16_t* w_norms, const DecodeParams& dw,
+                    int64_t n, int64_t m, int64_t d, void* Y, int y_bf16, int64_t ldy,
+                    hipStream_t stream);
+
+}  // namespace orbq

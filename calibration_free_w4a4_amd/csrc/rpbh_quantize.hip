@@ -1,0 +1,392 @@
+// rpbh_quantize: one pass over bf16 token rows that applies the RPBH rotation, takes the row
+// norm, normalises and quantizes every coordinate to a Lloyd-Max codebook, and packs the codes.
+//
+// Method: OrbitQuant summary (picx.dev), "Online Activation Quantization" (rotate, normalise,
+// quantize) and "Randomized Permuted Block-Hadamard (RPBH) Rotation"
+// (Pi = blkdiag(H_h D_i) P_pi, O(d log h) by the fast Walsh-Hadamard transform).  The same
+// kernel folds weight rows ("Offline Weight Quantization") with bf16 norms.
+//
+// Work layout (gfx950, wave64):
+//   * 32 consecutive post-permutation positions of one token per lane; a Hadamard block of
+//     h = 128 spans one quad of lanes (h = 64: a lane pair).  A workgroup holds `tg` tokens.
+//   * Each lane loads 32 consecutive input positions of its token (4 x 16-byte loads,
+//     coalesced across the lane's token), stores them to LDS and adds their squares into a
+//     partial norm (sum of squares is invariant under Pi).
+//   * After a barrier each lane gathers its 32 permuted positions from LDS with 16-bit
+//     reads, flips the Rademacher signs with one xor per bf16 pair, and runs the block FWHT:
+//     the first butterfly stage and the bf16 -> fp32 widening together with v_dot2_f32_bf16,
+//     the next four stages in registers, the last log2(h/32) stages across lanes with DPP.
+//   * Quantization uses the power-of-two-scaled coordinate t' = t * 2^k: one table lookup on
+//     floor(-t') and one fp32 compare give the exact nearest-centroid decision (QuantParams).
+//   * Codes are packed in registers and written with one 8/16/24-byte store per lane.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace orbq {
+namespace {
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kE = 32;  // positions per lane
+
+struct QuantKernelArgs {
+  const uint16_t* X;
+  int64_t n;
+  int64_t ldx;
+  const int32_t* perm;
+  const int8_t* signs;
+  uint8_t* codes;
+  void* norms;
+  float* x_rot;
+  int32_t d;
+  int32_t lpt;     // lanes per token = d / 32
+  int32_t tg;      // tokens per workgroup iteration
+  int32_t seg;     // power-of-two lane segment reduced with shuffles
+  int32_t nseg;    // segments per token
+  int32_t ngroups;
+  float eps;
+  float inv_scale; // 2^k / sqrt(h) (quantize) or 1 / sqrt(h) (rotate only)
+  QuantParams qp;
+};
+
+__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
+                                         0.0f, false);
+}
+
+// value of `x` in the lane whose index differs in bit 0 (xor 1) or bit 1 (xor 2) within the quad
+template <int XOR>
+__device__ __forceinline__ float quad_xor(float x) {
+  constexpr int ctrl = XOR == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
+}
+
+__device__ __forceinline__ int floor_neg_to_int(float x) {
+  int r;
+  asm("v_cvt_flr_i32_f32_e64 %0, -%1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+__device__ __forceinline__ uint16_t bf16_rne_dev(float x) {
+  uint32_t u = __builtin_bit_cast(uint32_t, x);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+// Builds the per-bucket table: entry for bucket j = floor(-t') in [-J, J-1] is
+// (threshold, base code); the code is base + (|t'| > threshold).
+__device__ void build_table(const QuantParams& qp, float2* tbl, int tid, int nthreads) {
+  const int J = qp.J, half = 1 << (qp.bits - 1);
+  for (int e = tid; e < 2 * J; e += nthreads) {
+    const int j = e - J;
+    float thr = __builtin_inff();
+    int base = 0;
+    if (j < 0) {  // t' in (i, i + 1], i = -j - 1
+      const float lo = static_cast<float>(-j - 1), hi = lo + 1.0f;
+      for (int p = 0; p < qp.nb; ++p) {
+        const float b = qp.thr_gt[p];
+        if (b <= lo) ++base;
+        else if (b < hi) thr = b;
+      }
+    } else {      // |t'| in [j, j + 1), t' <= 0
+      const float lo = static_cast<float>(j), hi = lo + 1.0f;
+      for (int p = 0; p < qp.nb; ++p) {
+        const float b = qp.thr_ge[p];
+        if (b < lo) ++base;
+        else if (b < hi) thr = b;
+      }
+      base += half;
+    }
+    tbl[e] = make_float2(thr, __builtin_bit_cast(float, base));
+  }
+}
+
+__device__ __forceinline__ uint32_t quantize_one(float tp, const float2* tbl, int J) {
+  int j = floor_neg_to_int(tp);
+  j = min(max(j, -J), J - 1);
+  const float2 e = tbl[j];  // tbl points at bucket 0
+  return static_cast<uint32_t>(__builtin_bit_cast(int, e.y)) + (__builtin_fabsf(tp) > e.x ? 1u : 0u);
+}
+
+template <int H, int BITS, QuantMode MODE>
+__global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int d = a.d;
+  uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                                    // [tg][d]
+  float2* tbl_all = reinterpret_cast<float2*>(smem + ((static_cast<size_t>(a.tg) * d * 2 + 15) & ~size_t(15)));
+  float* part = reinterpret_cast<float*>(tbl_all + 2 * a.qp.J);                       // [tg][nseg]
+  const int tid = threadIdx.x;
+  const int nact = a.tg * a.lpt;
+  const bool active = tid < nact;
+  const int slot = active ? tid / a.lpt : 0;
+  const int q = tid - slot * a.lpt;
+  const int J = a.qp.J;
+
+  if (MODE != QuantMode::kRotateOnly) build_table(a.qp, tbl_all, tid, blockDim.x);
+  const float2* tbl = tbl_all + J;
+
+  // loop-invariant gather addresses (LDS byte offsets) and sign masks of this lane's positions
+  uint32_t gaddr[kE];
+  uint32_t smask[kE / 2];
+  {
+    const int j0 = kE * q;
+    const uint32_t rowbase = static_cast<uint32_t>(slot * d);
+#pragma unroll
+    for (int i = 0; i < kE; ++i) {
+      int p = active ? a.perm[j0 + i] : 0;
+      p = min(max(p, 0), d - 1);
+      gaddr[i] = (rowbase + static_cast<uint32_t>(p)) * 2u;
+    }
+#pragma unroll
+    for (int i = 0; i < kE / 2; ++i) {
+      const int s0 = active ? a.signs[j0 + 2 * i] : 1, s1 = active ? a.signs[j0 + 2 * i + 1] : 1;
+      smask[i] = (s0 < 0 ? 0x8000u : 0u) | (s1 < 0 ? 0x80000000u : 0u);
+    }
+  }
+  // cross-lane butterflies leave the result negated in lanes with an odd number of "upper"
+  // positions; fold that sign into the per-token scale
+  constexpr int LPB = H / kE;  // lanes per Hadamard block
+  const float lane_sign = (__builtin_popcount(q & (LPB - 1)) & 1) ? -1.0f : 1.0f;
+  const float sgn1 = (q & 1) ? -1.0f : 1.0f;
+  const float sgn2 = (q & 2) ? -1.0f : 1.0f;
+  constexpr uint32_t kOnes = 0x3F803F80u;     // bf16 (1, 1)
+  constexpr uint32_t kPlusMinus = 0xBF803F80u; // bf16 (1, -1)
+
+  for (int g = blockIdx.x; g < a.ngroups; g += gridDim.x) {
+    const int64_t row = static_cast<int64_t>(g) * a.tg + slot;
+    const bool valid = active && row < a.n;
+
+    // ---- stage 32 input positions of this lane's token into LDS; partial sum of squares
+    uint4 v[4];
+    if (valid) {
+      const uint4* src = reinterpret_cast<const uint4*>(a.X + row * a.ldx + kE * q);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = src[c];
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) v[c] = make_uint4(0, 0, 0, 0);
+    }
+    __syncthreads();  // previous iteration's gathers are done with xs
+    float ss = 0.0f;
+    if (active) {
+      uint4* dst = reinterpret_cast<uint4*>(xs + slot * d + kE * q);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        dst[c] = v[c];
+        ss += dot2_bf16(v[c].x, v[c].x);
+        ss += dot2_bf16(v[c].y, v[c].y);
+        ss += dot2_bf16(v[c].z, v[c].z);
+        ss += dot2_bf16(v[c].w, v[c].w);
+      }
+    }
+    for (int off = 1; off < a.seg; off <<= 1) ss += __shfl_xor(ss, off, 64);
+    if (active && (q & (a.seg - 1)) == 0) part[slot * a.nseg + q / a.seg] = ss;
+    __syncthreads();
+    if (!active) continue;
+
+    // ---- gather the permuted positions, apply signs, FWHT stage 1 (+ widening to fp32)
+    float y[kE];
+#pragma unroll
+    for (int i = 0; i < kE / 2; ++i) {
+      u16x2_t pr;
+      pr.x = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i]);
+      pr.y = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i + 1]);
+      const uint32_t w = __builtin_bit_cast(uint32_t, pr) ^ smask[i];
+      y[2 * i] = dot2_bf16(w, kOnes);
+      y[2 * i + 1] = dot2_bf16(w, kPlusMinus);
+    }
+    // ---- FWHT stages 2..5 in registers
+#pragma unroll
+    for (int st = 2; st < kE; st <<= 1) {
+#pragma unroll
+      for (int i = 0; i < kE; ++i) {
+        if (i & st) continue;
+        const float u0 = y[i], u1 = y[i + st];
+        y[i] = u0 + u1;
+        y[i + st] = u0 - u1;
+      }
+    }
+    // ---- remaining stages across the lanes of the block: x += sgn * partner
+    if constexpr (LPB >= 2) {
+#pragma unroll
+      for (int i = 0; i < kE; ++i) y[i] = __builtin_fmaf(quad_xor<1>(y[i]), sgn1, y[i]);
+    }
+    if constexpr (LPB >= 4) {
+#pragma unroll
+      for (int i = 0; i < kE; ++i) y[i] = __builtin_fmaf(quad_xor<2>(y[i]), sgn2, y[i]);
+    }
+
+    // ---- token norm: the lane segments' partial sums, added in a fixed order
+    float s2 = 0.0f;
+    for (int k = 0; k < a.nseg; ++k) s2 += part[slot * a.nseg + k];
+    const float s = __builtin_sqrtf(s2);
+
+    if constexpr (MODE == QuantMode::kRotateOnly) {
+      if (!valid) continue;
+      const float sc = a.inv_scale * lane_sign;
+      float4* dst = reinterpret_cast<float4*>(a.x_rot + row * d + kE * q);
+#pragma unroll
+      for (int c = 0; c < kE / 4; ++c)
+        dst[c] = make_float4(y[4 * c] * sc, y[4 * c + 1] * sc, y[4 * c + 2] * sc, y[4 * c + 3] * sc);
+      if (q == 0) reinterpret_cast<float*>(a.norms)[row] = s;
+      continue;
+    } else {
+      const float inv = lane_sign * (a.inv_scale / (s + a.eps));
+      if (!valid) continue;
+      uint8_t* crow = a.codes + row * static_cast<int64_t>(d * BITS / 8) + q * (kE * BITS / 8);
+      if constexpr (BITS == 4) {
+        uint32_t w[4] = {0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < kE; ++i) w[i >> 3] |= quantize_one(y[i] * inv, tbl, J) << (4 * (i & 7));
+        *reinterpret_cast<uint4*>(crow) = make_uint4(w[0], w[1], w[2], w[3]);
+      } else if constexpr (BITS == 2) {
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < kE; ++i) w[i >> 4] |= quantize_one(y[i] * inv, tbl, J) << (2 * (i & 15));
+        *reinterpret_cast<uint2*>(crow) = make_uint2(w[0], w[1]);
+      } else {
+        uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+        for (int i = 0; i < kE; ++i) {
+          const uint32_t c = quantize_one(y[i] * inv, tbl, J);
+          const int bit = 6 * i, wi = bit >> 5, sh = bit & 31;
+          w[wi] |= c << sh;
+          if (sh > 26) w[wi + 1] |= c >> (32 - sh);
+        }
+        uint2* dst = reinterpret_cast<uint2*>(crow);
+        dst[0] = make_uint2(w[0], w[1]);
+        dst[1] = make_uint2(w[2], w[3]);
+        dst[2] = make_uint2(w[4], w[5]);
+      }
+      if (q == 0) {
+        if constexpr (MODE == QuantMode::kWeights)
+          reinterpret_cast<uint16_t*>(a.norms)[row] = bf16_rne_dev(s);
+        else
+          reinterpret_cast<float*>(a.norms)[row] = s;
+      }
+    }
+  }
+}
+
+__global__ void k_quantize_t(const float* t, int64_t count, QuantParams qp, uint8_t* codes) {
+  __shared__ float2 tbl_all[2 * kMaxTableHalf];
+  build_table(qp, tbl_all, threadIdx.x, blockDim.x);
+  __syncthreads();
+  const float2* tbl = tbl_all + qp.J;
+  for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
+       i += static_cast<int64_t>(gridDim.x) * blockDim.x)
+    codes[i] = static_cast<uint8_t>(quantize_one(t[i] * qp.scale, tbl, qp.J));
+}
+
+template <int H, int BITS, QuantMode MODE>
+hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, int grid, hipStream_t st) {
+  hipLaunchKernelGGL((k_rpbh_quantize<H, BITS, MODE>), dim3(grid), dim3(threads), lds, st, a);
+  return hipGetLastError();
+}
+
+template <int H, QuantMode MODE>
+hipError_t launch_bits(int bits, const QuantKernelArgs& a, int threads, size_t lds, int grid, hipStream_t st) {
+  switch (bits) {
+    case 2: return launch_typed<H, 2, MODE>(a, threads, lds, grid, st);
+    case 4: return launch_typed<H, 4, MODE>(a, threads, lds, grid, st);
+    default: return launch_typed<H, 6, MODE>(a, threads, lds, grid, st);
+  }
+}
+
+template <QuantMode MODE>
+hipError_t launch_mode(int block, int bits, const QuantKernelArgs& a, int threads, size_t lds, int grid,
+                       hipStream_t st) {
+  return block == 64 ? launch_bits<64, MODE>(bits, a, threads, lds, grid, st)
+                     : launch_bits<128, MODE>(bits, a, threads, lds, grid, st);
+}
+
+int device_cu_count() {
+  static thread_local int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached_dev = dev;
+    cached_cus = cus;
+  }
+  return cached_cus;
+}
+
+}  // namespace
+
+int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t ldx, const RotArgs& rot,
+                         const QuantParams* qp, float eps, uint8_t* codes, void* norms, float* x_rot,
+                         hipStream_t stream) {
+  QuantKernelArgs a{};
+  a.X = X;
+  a.n = n;
+  a.ldx = ldx;
+  a.perm = rot.perm;
+  a.signs = rot.signs;
+  a.codes = codes;
+  a.norms = norms;
+  a.x_rot = x_rot;
+  a.d = rot.d;
+  a.lpt = rot.d / kE;
+  a.eps = eps;
+  if (qp) a.qp = *qp;
+  else {
+    a.qp.J = 0;
+    a.qp.bits = 4;
+  }
+  // tokens per workgroup: least idle lanes, then the workgroup closest to 256 threads
+  int best_tg = 1, best_threads = 0;
+  double best_score = 1e30;
+  for (int tg = 1; tg * a.lpt <= 512; ++tg) {
+    const int act = tg * a.lpt, thr = (act + 63) / 64 * 64;
+    const double waste = static_cast<double>(thr - act) / thr;
+    const double score = waste * 10.0 + std::abs(std::log2(thr / 256.0)) * 0.01;
+    if (score < best_score) {
+      best_score = score;
+      best_tg = tg;
+      best_threads = thr;
+    }
+  }
+  a.tg = best_tg;
+  int seg = 1;
+  while (seg < 64 && (a.lpt % (seg * 2)) == 0) seg *= 2;
+  a.seg = seg;
+  a.nseg = a.lpt / seg;
+  a.ngroups = static_cast<int>((n + a.tg - 1) / a.tg);
+  const float rsqrt_h = 1.0f / __builtin_sqrtf(static_cast<float>(rot.block));
+  a.inv_scale = (mode == QuantMode::kRotateOnly) ? rsqrt_h : static_cast<float>(static_cast<double>(a.qp.scale) /
+                                                                                 std::sqrt(static_cast<double>(rot.block)));
+  const size_t lds = ((static_cast<size_t>(a.tg) * rot.d * 2 + 15) & ~size_t(15)) +
+                     sizeof(float2) * 2 * a.qp.J + sizeof(float) * a.tg * a.nseg;
+  // balanced persistent grid: every workgroup runs the same number of token groups
+  const int max_grid = device_cu_count() * 8;
+  const int iters = (a.ngroups + max_grid - 1) / max_grid;
+  const int grid = (a.ngroups + iters - 1) / iters;
+  hipError_t e;
+  const int bits = a.qp.bits;
+  switch (mode) {
+    case QuantMode::kActivations:
+      e = launch_mode<QuantMode::kActivations>(rot.block, bits, a, best_threads, lds, grid, stream);
+      break;
+    case QuantMode::kWeights:
+      e = launch_mode<QuantMode::kWeights>(rot.block, bits, a, best_threads, lds, grid, stream);
+      break;
+    default:
+      e = launch_mode<QuantMode::kRotateOnly>(rot.block, 4, a, best_threads, lds, grid, stream);
+      break;
+  }
+  return static_cast<int>(e);
+}
+
+int launch_quantize_t(const float* t, int64_t count, const QuantParams& qp, uint8_t* codes, hipStream_t stream) {
+  const int threads = 256;
+  int64_t blocks = (count + threads - 1) / threads;
+  if (blocks > 4096) blocks = 4096;
+  hipLaunchKernelGGL(k_quantize_t, dim3(static_cast<unsigned>(blocks)), dim3(threads), 0, stream, t, count, qp, codes);
+  return static_cast<int>(hipGetLastError());
+}
+
+}  // namespace orbq

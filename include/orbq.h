@@ -1,0 +1,173 @@
+/*
+ * orbq.h -- C ABI of the OrbitQuant quantized linear layer on AMD Instinct MI355X (gfx950).
+ *
+ * What the library computes (OrbitQuant summary, picx.dev, "Methodology"):
+ *   offline  "Offline Weight Quantization": W' = W Pi^T, r'_i = ||w'_i||, codes of
+ *            w'_i / r'_i under a Lloyd-Max codebook, r' stored in bf16.
+ *   online   "Online Activation Quantization": x' = Pi x, s = ||x'||, codes of
+ *            x' / (s + eps) under a Lloyd-Max codebook; the product with the folded
+ *            weights needs no inverse rotation because Pi^T Pi = I.
+ *   Pi       "Randomized Permuted Block-Hadamard (RPBH) Rotation":
+ *            Pi = blkdiag(H_h D_1, ..., H_h D_{d/h}) P_pi.
+ *   codebook "Theoretical Basis" item 2: Lloyd-Max centroids for the marginal f_d of a
+ *            rotated unit vector (item 1); one codebook per (d, bits), shared by all
+ *            layers and by weights and activations ("Data-Agnostic Codebook").
+ *
+ * Conventions fixed here where the pages are silent:
+ *   - H_h is the Sylvester (natural order) Hadamard matrix scaled by 1/sqrt(h), so Pi is
+ *     orthogonal.  (P_pi x)[j] = x[perm[j]]; signs[j] multiplies position j after the
+ *     permutation.
+ *   - Quantization is q(t) = argmin_k |t - c_k| over the ascending codebook, ties to the
+ *     lower index k; t = x' / (s + eps) with the unrounded norm.
+ *   - Code value (sign-magnitude): for N = 2^bits centroids, centroid k >= N/2 is stored
+ *     as k - N/2 and centroid k < N/2 as N/2 + (N/2 - 1 - k): the top bit is the sign
+ *     (1 = negative), the low bits rank |c_k| from the smallest magnitude up.
+ *   - Packed rows: the d codes of a row in order, rows back to back, d*bits/8 bytes per
+ *     row, least significant bits first:
+ *        bits = 4: code j in byte j/2, bits 4*(j%2)..+3
+ *        bits = 2: code j in byte j/4, bits 2*(j%4)..+1
+ *        bits = 6: code j in the 3-byte little-endian group j/4, bits 6*(j%4)..+5
+ *   - The product decodes each centroid to bf16 (round to nearest even), multiplies in
+ *     bf16 with fp32 accumulation, and scales by s_i (fp32) and r'_j (bf16) in fp32.
+ *
+ * Memory: every buffer is owned by the caller.  Pointers marked [device] are HIP device
+ * pointers, [host] are host pointers.  The library allocates no device memory: the
+ * workspace of orbq_linear comes from the caller.  Calls are asynchronous on `stream`
+ * (a hipStream_t; NULL = the default stream) and re-entrant; argument errors are
+ * detected on the host before anything is launched and are returned synchronously.
+ * Device faults surface at the caller's next synchronisation.  Device arrays (perm,
+ * signs) are read, never validated, by the kernels: a perm entry outside [0, d) is
+ * clamped into range (garbage in, garbage out, no out-of-bounds access).
+ *
+ * Supported shapes: block in {64, 128}; d a multiple of block and at most 16384;
+ * activation bits and weight bits each in {2, 4, 6}.  n or m equal to 0 is a no-op.
+ * Alignment: bf16 matrices and code buffers 16-byte aligned with row pitches that
+ * are multiples of 16 bytes; norm arrays 4-byte (fp32) or 2-byte (bf16) aligned;
+ * Y 16-byte aligned with a row pitch that is a multiple of 16 bytes.
+ */
+#ifndef ORBQ_H
+#define ORBQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  ORBQ_OK = 0,
+  ORBQ_ERR_INVALID_ARG = -1,  /* null pointer, bad size, ld < d, n/m/d negative        */
+  ORBQ_ERR_UNSUPPORTED = -2,  /* block, bits or d outside the supported set            */
+  ORBQ_ERR_ALIGNMENT = -3,    /* pointer or pitch not aligned as documented above      */
+  ORBQ_ERR_WORKSPACE = -4,    /* workspace smaller than orbq_linear_workspace_bytes    */
+  ORBQ_ERR_HIP = -5,          /* a HIP runtime call failed (launch, device query)      */
+  ORBQ_ERR_CODEBOOK = -6      /* codebook not ascending, not antisymmetric, not finite */
+} orbq_status;
+
+typedef enum { ORBQ_F32 = 0, ORBQ_BF16 = 1 } orbq_dtype;
+
+/* RPBH rotation for one dimension d (OrbitQuant summary, "Randomized Permuted
+ * Block-Hadamard (RPBH) Rotation"; fixed once per dimension).
+ *   d      dimension, multiple of block
+ *   block  Hadamard block size h (64 or 128)
+ *   perm   [device] int32[d], a permutation of 0..d-1: (P x)[j] = x[perm[j]]
+ *   signs  [device] int8[d], each +1 or -1, applied to position j after the permutation */
+typedef struct {
+  int32_t d;
+  int32_t block;
+  const int32_t* perm;
+  const int8_t* signs;
+} orbq_rpbh;
+
+/* Lloyd-Max codebook for (d, bits) ("Theoretical Basis" item 2).
+ *   centroids  [host] float[2^bits], strictly ascending, exactly antisymmetric
+ *              (c[N-1-k] == -c[k]), in units of the normalised coordinate t. */
+typedef struct {
+  int32_t d;
+  int32_t bits;
+  const float* centroids;
+} orbq_codebook;
+
+/* Offline, host only.  Lloyd-Max centroids of f_d(t) ~ (1 - t^2)^((d-3)/2) on [-1, 1]
+ * ("Theoretical Basis" items 1-2; TurboQuant slides, docswell, "Page. 13"-"Page. 16"),
+ * by Lloyd iteration with Gauss-Legendre cell integrals in float64, rounded to float32.
+ * centroids_out [host] receives 2^bits floats.  bits in 1..8, d >= 3.
+ * Returns ORBQ_OK or ORBQ_ERR_INVALID_ARG. */
+int orbq_codebook_lloyd_max(int32_t d, int32_t bits, float* centroids_out);
+
+/* Host only, O(d): checks that perm_host is a permutation of 0..d-1, signs_host holds only
+ * +1/-1, block is supported and divides d.  Use it on the host copies before uploading. */
+int orbq_rpbh_validate(int32_t d, int32_t block, const int32_t* perm_host, const int8_t* signs_host);
+
+/* Host only: checks a codebook as every entry point does (see ORBQ_ERR_CODEBOOK). */
+int orbq_codebook_validate(const orbq_codebook* cb);
+
+/* Bytes of one packed code row: d*bits/8.  0 if d*bits is not a multiple of 8. */
+size_t orbq_codes_row_bytes(int64_t d, int32_t bits);
+
+/* Offline weight fold and quantize ("Offline Weight Quantization", steps 1-4).
+ *   W          [device] bf16[m][ldw] (row-major; row i is w_i), ldw >= d
+ *   rot, cb_w  rotation and weight codebook for dimension d (cb_w->d == d == rot->d)
+ *   eps        added to the row norm before dividing (the page writes no eps for weights;
+ *              1e-8 keeps zero rows finite)
+ *   w_codes    [device] uint8[m][d*bits/8], packed codes of Q(w'_i / (r'_i + eps))
+ *   w_norms    [device] bf16[m], r'_i = ||Pi w_i|| rounded to nearest even
+ * The same kernel as orbq_rpbh_quantize, with bf16 norms. */
+int orbq_fold_weights(const void* W, int64_t m, int64_t d, int64_t ldw, const orbq_rpbh* rot,
+                      const orbq_codebook* cb_w, float eps, uint8_t* w_codes, void* w_norms,
+                      void* stream);
+
+/* Online activation quantization ("Online Activation Quantization", steps 1-3).
+ *   X          [device] bf16[n][ldx], token rows, ldx >= d
+ *   x_codes    [device] uint8[n][d*bits/8], packed codes of Q(x'_i / (s_i + eps))
+ *   x_norms    [device] float[n], s_i = ||Pi x_i|| in fp32
+ * One pass over X: permute, sign, block FWHT, norm, threshold, pack. */
+int orbq_rpbh_quantize(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                       const orbq_codebook* cb_a, float eps, uint8_t* x_codes, float* x_norms,
+                       void* stream);
+
+/* Product in the rotated basis ("Online Activation Quantization", last paragraph: the
+ * rotations cancel):  Y[i][j] = s_i * r'_j * sum_k bf16(C_a[a_ik]) * bf16(C_w[w_jk]).
+ *   x_codes, x_norms   [device] as written by orbq_rpbh_quantize (n rows)
+ *   w_codes, w_norms   [device] as written by orbq_fold_weights (m rows)
+ *   Y                  [device] float or bf16 [n][ldy], ldy >= m
+ * bf16 MFMA with fp32 accumulation; the epilogue scales in fp32 and rounds to y_type. */
+int orbq_lut_gemm(const uint8_t* x_codes, const float* x_norms, const orbq_codebook* cb_a,
+                  const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w,
+                  int64_t n, int64_t m, int64_t d, void* Y, orbq_dtype y_type, int64_t ldy,
+                  void* stream);
+
+/* Workspace bytes orbq_linear needs for n tokens of dimension d at bits_a: packed codes
+ * (rounded up to 256 bytes) followed by n fp32 norms. */
+size_t orbq_linear_workspace_bytes(int64_t n, int64_t d, int32_t bits_a);
+
+/* The online layer: orbq_rpbh_quantize into `workspace`, then orbq_lut_gemm, on one
+ * stream.  Arguments as in those two calls; ws_bytes >= orbq_linear_workspace_bytes. */
+int orbq_linear(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
+                const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes, void* Y,
+                orbq_dtype y_type, int64_t ldy, void* stream);
+
+/* Human-readable name of a status code, and the detail of the last error on this thread. */
+const char* orbq_status_string(int status);
+const char* orbq_last_error(void);
+
+/* ---- test-only entry points (stable names, not part of the layer's contract) ---- */
+
+/* x' = Pi x in fp32 [n][d] (the FWHT output scaled by 1/sqrt(block)) and s_i as
+ * orbq_rpbh_quantize computes it: exposes the rotation alone for checking. */
+int orbq_test_rotate(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                     float* x_rot, float* x_norms, void* stream);
+
+/* Quantize `count` given fp32 values t (already normalised) with the decision the kernels
+ * use; writes one sign-magnitude code per byte.  cb->d selects nothing here but is
+ * validated like elsewhere. */
+int orbq_test_quantize_t(const float* t, int64_t count, const orbq_codebook* cb, uint8_t* codes,
+                         void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* ORBQ_H */

@@ -23,7 +23,7 @@ from scipy.stats import norm
 from .density import cell_mass, cell_moment
 
 
-def lloyd_max(d: int, bits: int, tol: float = 1e-13, max_iter: int = 2_000_000,
+def lloyd_max(d: int, bits: int, tol: float = 1e-15, max_iter: int = 2_000_000,
               return_iters: bool = False):
     """2^bits float64 centroids, ascending and exactly antisymmetric."""
     n_lv = 1 << bits

@@ -1,0 +1,149 @@
+"""CPU tests of the C-ABI library: it loads, exports what include/orbq.h declares, its
+host-only calls work, and every argument error is caught before anything is launched.
+No GPU is needed: no call here reaches a kernel."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+import calibration_free_w4a4_amd as orbq
+import oracle
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "orbq.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(orbq.library_path()), reason="liborbq.so not built")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(orbq_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    lib = ctypes.CDLL(orbq.library_path())
+    names = declared_functions()
+    assert len(names) >= 13
+    for name in names:
+        assert hasattr(lib, name), name
+    assert set(names) == set(orbq._SIGS), "binding signatures out of sync with the header"
+
+
+@pytest.mark.parametrize("d,bits", [(256, 4), (3072, 4), (3072, 2), (12288, 4), (1536, 6), (8960, 6),
+                                    (1536, 4), (8960, 4)])
+def test_library_codebook_matches_oracle(d, bits, cb):
+    lib_c = orbq.Codebook.lloyd_max(d, bits).centroids
+    ref = oracle.lloyd_max(d, bits)
+    assert np.max(np.abs(lib_c.astype(np.float64) - ref) / np.abs(ref)) < 1e-6   # fp32 rounding
+    # both converge to the unique optimum (f_d is log-concave): the fp32 codebooks coincide
+    assert np.array_equal(lib_c, cb(d, bits))
+
+
+def test_library_codebook_float64_agreement():
+    """The library's float64 iterate agrees with the oracle's far below fp32 resolution:
+    checked through the fp32 result of a 1-bit codebook, whose value has a closed form."""
+    c = orbq.Codebook.lloyd_max(3072, 1).centroids
+    assert c[1] == np.float32(oracle.mean_abs_t(3072)) and c[0] == -c[1]
+
+
+def test_rpbh_validate():
+    lib = orbq.load()
+    d = 256
+    perm = np.random.default_rng(0).permutation(d).astype(np.int32)
+    signs = np.ones(d, np.int8)
+    assert lib.orbq_rpbh_validate(d, 64, perm.ctypes.data, signs.ctypes.data) == 0
+    bad = perm.copy(); bad[3] = bad[4]
+    assert lib.orbq_rpbh_validate(d, 64, bad.ctypes.data, signs.ctypes.data) == -1
+    bad = perm.copy(); bad[0] = d
+    assert lib.orbq_rpbh_validate(d, 64, bad.ctypes.data, signs.ctypes.data) == -1
+    s2 = signs.copy(); s2[7] = 0
+    assert lib.orbq_rpbh_validate(d, 64, perm.ctypes.data, s2.ctypes.data) == -1
+    assert lib.orbq_rpbh_validate(d, 32, perm.ctypes.data, signs.ctypes.data) == -2
+    assert lib.orbq_rpbh_validate(192, 128, perm.ctypes.data, signs.ctypes.data) == -1
+
+
+def _cb_struct(c, d, bits):
+    c = np.ascontiguousarray(c, np.float32)
+    return orbq._Codebook(d, bits, c.ctypes.data_as(ctypes.POINTER(ctypes.c_float))), c
+
+
+def test_codebook_validate(cb):
+    lib = orbq.load()
+    good = cb(256, 4)
+    s, keep = _cb_struct(good, 256, 4)
+    assert lib.orbq_codebook_validate(ctypes.byref(s)) == 0
+    for broken in (good[::-1].copy(), np.where(np.arange(16) == 3, good * 1.0001, good)):
+        s, keep = _cb_struct(broken, 256, 4)
+        assert lib.orbq_codebook_validate(ctypes.byref(s)) == -6
+    nan = good.copy(); nan[5] = np.nan
+    s, keep = _cb_struct(nan, 256, 4)
+    assert lib.orbq_codebook_validate(ctypes.byref(s)) == -6
+    s, keep = _cb_struct(cb(256, 4), 256, 3)
+    assert lib.orbq_codebook_validate(ctypes.byref(s)) == -2
+
+
+def test_sizes():
+    lib = orbq.load()
+    assert lib.orbq_codes_row_bytes(3072, 4) == 1536
+    assert lib.orbq_codes_row_bytes(3072, 2) == 768
+    assert lib.orbq_codes_row_bytes(8960, 6) == 6720
+    assert lib.orbq_codes_row_bytes(3, 2) == 0
+    ws = lib.orbq_linear_workspace_bytes(4608, 3072, 4)
+    assert ws == ((4608 * 1536 + 255) // 256) * 256 + 4608 * 4
+    assert lib.orbq_linear_workspace_bytes(10, 3072, 3) == 0
+
+
+def test_status_strings():
+    lib = orbq.load()
+    for code, name in ((0, b"ORBQ_OK"), (-1, b"ORBQ_ERR_INVALID_ARG"), (-4, b"ORBQ_ERR_WORKSPACE"),
+                       (-6, b"ORBQ_ERR_CODEBOOK")):
+        assert lib.orbq_status_string(code) == name
+
+
+def test_argument_errors_return_before_launch(cb):
+    """Every argument error is reported synchronously with its status; none needs a GPU."""
+    lib = orbq.load()
+    d = 256
+    c4, keep4 = _cb_struct(cb(d, 4), d, 4)
+    rot = orbq._Rpbh(d, 64, 0x1000, 0x2000)     # device arrays are never dereferenced on the host
+    P = 0x10000                                  # a 16-byte aligned dummy device address
+    q = lib.orbq_rpbh_quantize
+    # bad shapes / arguments
+    assert q(P, 8, d, d - 1, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, None) == -1      # ld < d
+    assert q(P, -1, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, None) == -1         # n < 0
+    assert q(None, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, None) == -1       # NULL X
+    assert q(P + 2, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, None) == -3      # misaligned
+    assert q(P, 8, d, d + 4, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, None) == -3      # pitch
+    assert q(P, 8, d, d, None, ctypes.byref(c4), 1e-8, P, P, None) == -1                       # no rotation
+    assert q(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), float("nan"), P, P, None) == -1  # eps
+    rot32 = orbq._Rpbh(d, 32, 0x1000, 0x2000)
+    assert q(P, 8, d, d, ctypes.byref(rot32), ctypes.byref(c4), 1e-8, P, P, None) == -2        # block
+    c4d, keep = _cb_struct(cb(d, 4), 512, 4)
+    assert q(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4d), 1e-8, P, P, None) == -1         # codebook d
+    c3, keep3 = _cb_struct(np.linspace(-1, 1, 8), d, 3)
+    assert q(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c3), 1e-8, P, P, None) == -2          # bits
+    assert "ld" in lib.orbq_last_error().decode() or lib.orbq_last_error()
+    # n == 0 is a no-op that succeeds without touching the device
+    assert q(None, 0, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, None, None, None) == 0
+    # gemm
+    g = lib.orbq_lut_gemm
+    assert g(P, P, ctypes.byref(c4), P, P, ctypes.byref(c4), 8, 8, d, P, 0, 4, None) == -1       # ldy < m
+    assert g(P, P, ctypes.byref(c4), P, P, ctypes.byref(c4), 8, 8, d, P + 4, 0, 8, None) == -3   # Y misaligned
+    assert g(P, P, ctypes.byref(c4), P, P, ctypes.byref(c4), 8, 4, d, P, 0, 6, None) == -3       # fp32 pitch
+    assert g(P, P, ctypes.byref(c4), P, P, ctypes.byref(c4), 8, 8, d, P, 7, 8, None) == -1       # y_type
+    assert g(P, P, ctypes.byref(c4), P, P, ctypes.byref(c4), 0, 8, d, P, 0, 8, None) == 0        # empty
+    # linear workspace
+    ln = lib.orbq_linear
+    need = lib.orbq_linear_workspace_bytes(8, d, 4)
+    assert ln(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, ctypes.byref(c4), 8, P, need - 1,
+              P, 0, 8, None) == -4
+    assert ln(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, ctypes.byref(c4), 8, None, need,
+              P, 0, 8, None) == -4
+    assert ln(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, ctypes.byref(c4), 8, P + 16, need,
+              P, 0, 8, None) == -3
+    # quantize_t
+    assert lib.orbq_test_quantize_t(P, -1, ctypes.byref(c4), P, None) == -1
+    assert lib.orbq_test_quantize_t(P, 0, ctypes.byref(c4), P, None) == 0

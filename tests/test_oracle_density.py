@@ -10,6 +10,7 @@ import pytest
 from scipy import integrate
 
 import oracle
+import oracle.density
 
 DIMS = [64, 256, 1536, 3072, 8960, 12288]
 
@@ -68,3 +69,14 @@ def test_gaussian_limit_approach():
     scaled = errs * np.array(DIMS)
     assert scaled.max() / scaled.min() < 1.5
     assert errs[0] < 0.02            # "approximated by N(0, 1/d)" already at d = 64
+
+
+@pytest.mark.parametrize("d", [4, 64, 256, 1536, 3072, 8960, 12288])
+def test_gamma_ratio_against_exact_rationals(d):
+    """log Gamma(d/2) - log Gamma((d-1)/2) for even d = 2m: Gamma(m) / Gamma(m - 1/2)
+    = ((m-1)!)^2 4^(m-1) / ((2m-2)! sqrt(pi)), evaluated as an exact rational."""
+    from fractions import Fraction
+    m = d // 2
+    r = Fraction(math.factorial(m - 1) ** 2 * 4 ** (m - 1), math.factorial(2 * m - 2))
+    exact = math.log(float(r)) - 0.5 * math.log(math.pi)
+    assert abs(oracle.density.log_gamma_ratio_half((d - 1) / 2.0) - exact) < 2e-15
