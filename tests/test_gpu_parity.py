@@ -1,0 +1,274 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle on seeded inputs.
+
+Tolerances (north star of this layer):
+  * codes bit-exact except coordinates within 1e-5 (t units) of a decision boundary,
+    counted, at most 1e-5 of all coordinates;
+  * product from identical codes within 2e-3 max error relative to s_i r'_j sum|C_a C_w|
+    (fp32 accumulation gives ~1e-6);
+  * s within 1e-6 relative; r' equal to the oracle's bf16 or one bf16 ulp away when the
+    exact norm sits within 1e-6 (relative) of a bf16 rounding midpoint.
+"""
+import math
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from tests.conftest import oracle_codebook
+from tests.gpu_common import (check_codes, dense_pi, dev_bf16, gemm_error, host_bits, log, torch_mod)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def orbq():
+    torch = torch_mod()
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    import calibration_free_w4a4_amd as m
+    m.load()
+    return m
+
+
+def gpu_codebook(orbq, d, bits):
+    cb = orbq.Codebook.lloyd_max(d, bits)
+    ref = oracle_codebook(d, bits)
+    assert np.array_equal(cb.centroids, ref), "library and oracle codebooks differ"
+    return cb, ref
+
+
+def gpu_rotation(orbq, d, h):
+    perm, signs = workloads.rotation(d)
+    return orbq.Rotation.create(d, h, perm, signs)
+
+
+# ----------------------------------------------------------------- decision rule
+@pytest.mark.parametrize("d,bits", [(256, 4), (3072, 4), (3072, 2), (1536, 6), (8960, 6), (12288, 4)])
+def test_quantize_t_exact(orbq, d, bits):
+    """The kernels' decision on given fp32 t equals the oracle's exact argmin, bit for bit,
+    including every boundary, its fp32 neighbours, zeros, denormals and far tails."""
+    torch = torch_mod()
+    log(f"quantize_t d={d} bits={bits}")
+    cb, c = gpu_codebook(orbq, d, bits)
+    m = oracle.thresholds_midpoint(c)
+    probes = [np.float32(x) for x in (0.0, -0.0, 1e-45, -1e-45, 1e-38, -1e-38, 1.0, -1.0, 0.999, -0.999)]
+    for mid in m:
+        f = np.float32(mid)
+        for k in range(-3, 4):
+            probes.append(np.float32(f + k * np.spacing(f)) if k else f)
+    t = np.concatenate([np.array(probes, np.float32), c,
+                        (np.random.default_rng(d).standard_normal(200000) / math.sqrt(d)).astype(np.float32),
+                        np.linspace(-2 * c[-1], 2 * c[-1], 100001, dtype=np.float32)])
+    got = orbq.test_quantize_t(torch.from_numpy(t).cuda(), cb).cpu().numpy().astype(np.int64)
+    ref = oracle.to_sign_magnitude(oracle.argmin_codes(t.astype(np.float64), c), bits)
+    bad = np.nonzero(got != ref)[0]
+    assert bad.size == 0, f"{bad.size} decisions differ, first t={t[bad[:5]]} gpu={got[bad[:5]]} ref={ref[bad[:5]]}"
+
+
+# ----------------------------------------------------------------- rotation
+@pytest.mark.parametrize("d,h,n", [(256, 64, 64), (3072, 128, 19), (1536, 128, 9), (8960, 128, 5),
+                                   (12288, 128, 3), (384, 128, 7)])
+def test_rotation_matches_dense_matrix(orbq, d, h, n):
+    log(f"rotate d={d} h={h} n={n}")
+    rot = gpu_rotation(orbq, d, h)
+    X = workloads.activations(n, d, seed=1000 + d, kind="heavy", outlier_frac=0.002)
+    xr, s = orbq.test_rotate(dev_bf16(X), rot)
+    xr, s = xr.cpu().numpy().astype(np.float64), s.cpu().numpy().astype(np.float64)
+    Xf = workloads.f64_from_bf16_bits(X)
+    ref = oracle.rotate(Xf, dense_pi(d, h))
+    nrm = np.linalg.norm(Xf, axis=1)
+    err = np.abs(xr - ref) / nrm[:, None]
+    assert err.max() < 1e-5, err.max()
+    assert np.sqrt(np.mean(err ** 2)) < 1e-6
+    assert np.max(np.abs(s - nrm) / nrm) < 1e-6
+
+
+# ----------------------------------------------------------------- quantize / fold
+def _quant_case(orbq, name, rows=None, sample=None, weights=False):
+    torch = torch_mod()
+    L = workloads.CONFIGS[name]
+    bits = L.bits_w if weights else L.bits_a
+    X, W = workloads.layer_inputs(L, rows=rows)
+    src = W if weights else X
+    log(f"quantize {name} weights={weights} shape={src.shape} bits={bits}")
+    rot = gpu_rotation(orbq, L.d, L.block)
+    cb, c = gpu_codebook(orbq, L.d, bits)
+    dsrc = dev_bf16(src)
+    if weights:
+        codes, norms = orbq.fold_weights(dsrc, rot, cb)
+    else:
+        codes, norms = orbq.rpbh_quantize(dsrc, rot, cb)
+    torch.cuda.synchronize()
+    codes = codes.cpu().numpy()
+    norms = (norms.float() if weights else norms).cpu().numpy().astype(np.float64)
+    idx = np.arange(src.shape[0]) if sample is None else sample(src.shape[0])
+    Sf = workloads.f64_from_bf16_bits(src[idx])
+    Pi = dense_pi(L.d, L.block)
+    k_ref, s_ref, T_ref = oracle.quantize_activations(Sf, Pi, c)
+    k_gpu = oracle.unpack_codes(codes[idx], bits, L.d)
+    check_codes(k_gpu, k_ref, T_ref, c, f"{name} codes")
+    if weights:
+        r_ref = oracle.bf16_rne(s_ref)
+        diff = norms[idx] != r_ref
+        if diff.any():
+            ulp = 2.0 ** (np.floor(np.log2(r_ref[diff])) - 7)
+            assert np.all(np.abs(norms[idx][diff] - r_ref[diff]) <= ulp)
+            mid = r_ref[diff] + np.sign(norms[idx][diff] - r_ref[diff]) * ulp / 2
+            assert np.all(np.abs(s_ref[diff] - mid) <= 1e-6 * s_ref[diff])
+    else:
+        assert np.max(np.abs(norms[idx] - s_ref) / s_ref) < 1e-6
+    return codes, norms
+
+
+def _sample_rows(n, k=48, seed=0):
+    rng = np.random.default_rng(seed)
+    return np.unique(np.concatenate([[0, n - 1, n // 2], rng.choice(n, size=min(k, n), replace=False)]))
+
+
+def test_quantize_tiny_full(orbq):
+    _quant_case(orbq, "tiny")
+
+
+def test_fold_tiny_full(orbq):
+    _quant_case(orbq, "tiny", weights=True)
+
+
+@pytest.mark.parametrize("name,rows", [("flux_qkv", 515), ("flux_mlp_up_w2a4", 130), ("wan_ffn_up", 257),
+                                       ("wan_ffn_down", 67), ("flux_mlp_down", 33)])
+def test_quantize_ragged_full_compare(orbq, name, rows):
+    """Several workgroups and a ragged last group, every coordinate compared."""
+    _quant_case(orbq, name, rows=rows)
+
+
+@pytest.mark.parametrize("name", ["flux_qkv", "flux_mlp_up_w2a4", "wan_ffn_up"])
+def test_fold_weights_sampled(orbq, name):
+    _quant_case(orbq, name, weights=True, sample=lambda n: _sample_rows(n, 40, 1))
+
+
+# ----------------------------------------------------------------- product
+def _gemm_case(orbq, n, m, d, ba, bw, out_bf16=False, seed=7, sample=None):
+    torch = torch_mod()
+    log(f"gemm n={n} m={m} d={d} A{ba} W{bw} bf16={out_bf16}")
+    ca_cb, ca = gpu_codebook(orbq, d, ba)
+    cw_cb, cw = gpu_codebook(orbq, d, bw)
+    xb = workloads.random_code_bytes(n, d * ba // 8, seed)
+    wb = workloads.random_code_bytes(m, d * bw // 8, seed + 1)
+    s = workloads.random_norms(n, seed + 2).astype(np.float32)
+    r_bits = workloads.bf16_bits_from_f64(workloads.random_norms(m, seed + 3, 0.01, 0.1))
+    Y = orbq.lut_gemm(torch.from_numpy(xb).cuda(), torch.from_numpy(s).cuda(), ca_cb,
+                      torch.from_numpy(wb).cuda(), dev_bf16(r_bits), cw_cb, d,
+                      out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    Yh = (Y.float() if out_bf16 else Y).cpu().numpy().astype(np.float64)
+    r = workloads.f64_from_bf16_bits(r_bits)
+    la, lw = oracle.decode_lut_bf16(ca), oracle.decode_lut_bf16(cw)
+    if sample is None:
+        A = la[oracle.unpack_codes(xb, ba, d)]
+        B = lw[oracle.unpack_codes(wb, bw, d)]
+        e = gemm_error(Yh, A, B, s.astype(np.float64), r)
+    else:
+        ii, jj = sample
+        A = la[oracle.unpack_codes(xb[ii], ba, d)]
+        B = lw[oracle.unpack_codes(wb[jj], bw, d)]
+        e = gemm_error(Yh[np.ix_(ii, jj)], A, B, s[ii].astype(np.float64), r[jj])
+    log(f"  max relative error {e:.3g}")
+    tol = 2e-3 + (2.0 ** -8 if out_bf16 else 0.0)
+    assert e <= tol
+    return e
+
+
+@pytest.mark.parametrize("ba,bw", [(4, 4), (4, 2), (6, 4), (2, 2), (6, 6), (2, 6)])
+def test_lut_gemm_tiny_all_bit_pairs(orbq, ba, bw):
+    assert _gemm_case(orbq, 64, 256, 256, ba, bw) < 1e-5
+
+
+@pytest.mark.parametrize("out_bf16", [False, True])
+def test_lut_gemm_ragged(orbq, out_bf16):
+    """Ragged n and m (partial tiles on both axes), several K tiles."""
+    _gemm_case(orbq, 300, 520, 3072, 4, 4, out_bf16=out_bf16)
+
+
+def test_lut_gemm_from_oracle_codes(orbq):
+    """The product of codes the oracle produced from real activations and weights."""
+    torch = torch_mod()
+    L = workloads.CONFIGS["tiny"]
+    X, W = workloads.layer_inputs(L)
+    Pi = dense_pi(L.d, L.block)
+    cb, c = gpu_codebook(orbq, L.d, 4)
+    kx, s, _ = oracle.quantize_activations(workloads.f64_from_bf16_bits(X), Pi, c)
+    kw, r, _, _ = oracle.fold_weights(workloads.f64_from_bf16_bits(W), Pi, c)
+    Y = orbq.lut_gemm(torch.from_numpy(oracle.pack_codes(kx, 4)).cuda(),
+                      torch.from_numpy(s.astype(np.float32)).cuda(), cb,
+                      torch.from_numpy(oracle.pack_codes(kw, 4)).cuda(),
+                      dev_bf16(workloads.bf16_bits_from_f64(r)), cb, L.d)
+    lut = oracle.decode_lut_bf16(c)
+    e = gemm_error(Y.cpu().numpy().astype(np.float64), lut[kx], lut[kw],
+                   s.astype(np.float32).astype(np.float64), r)
+    assert e < 1e-5
+
+
+# ----------------------------------------------------------------- the layer
+def test_linear_equals_quantize_then_gemm(orbq):
+    torch = torch_mod()
+    L = workloads.CONFIGS["tiny"]
+    X, W = workloads.layer_inputs(L)
+    rot = gpu_rotation(orbq, L.d, L.block)
+    cb, c = gpu_codebook(orbq, L.d, 4)
+    dX, dW = dev_bf16(X), dev_bf16(W)
+    wc, wn = orbq.fold_weights(dW, rot, cb)
+    Y = orbq.linear(dX, rot, cb, wc, wn, cb)
+    xc, xs = orbq.rpbh_quantize(dX, rot, cb)
+    Y2 = orbq.lut_gemm(xc, xs, cb, wc, wn, cb, L.d)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    # against the oracle chain end to end (codes may flip at boundaries)
+    Pi = dense_pi(L.d, L.block)
+    kw, r, _, _ = oracle.fold_weights(workloads.f64_from_bf16_bits(W), Pi, c)
+    Yo, kx, s = oracle.orbq_linear(workloads.f64_from_bf16_bits(X), Pi, c, kw, r, c)
+    lut = oracle.decode_lut_bf16(c)
+    den = (np.abs(lut[kx]) @ np.abs(lut[kw]).T) * s[:, None] * r[None, :]
+    e = np.max(np.abs(Y.cpu().numpy() - Yo) / den)
+    log(f"  linear vs oracle chain: {e:.3g}")
+    assert e < 2e-3
+    # quantization error of the whole layer against the unquantized product (informational bound)
+    ref = workloads.f64_from_bf16_bits(X) @ workloads.f64_from_bf16_bits(W).T
+    rel = np.linalg.norm(Y.cpu().numpy() - ref) / np.linalg.norm(ref)
+    log(f"  ||Y - XW^T|| / ||XW^T|| = {rel:.4f}")
+    assert rel < 0.3
+
+
+# ----------------------------------------------------------------- edge cases
+def test_edge_cases(orbq):
+    torch = torch_mod()
+    d, h = 256, 64
+    rot = gpu_rotation(orbq, d, h)
+    cb, c = gpu_codebook(orbq, d, 4)
+    # zero rows, a constant row, a single outlier, and n = 1
+    X = np.zeros((5, d))
+    X[1] = 1.0
+    X[2, 17] = 1000.0
+    X[3] = np.linspace(-1, 1, d)
+    X[4] = -0.0
+    bits = workloads.bf16_bits_from_f64(X)
+    bits[4] = 0x8000                       # -0.0 everywhere
+    codes, s = orbq.rpbh_quantize(dev_bf16(bits), rot, cb)
+    k = oracle.unpack_codes(codes.cpu().numpy(), 4, d)
+    k_ref, s_ref, T = oracle.quantize_activations(workloads.f64_from_bf16_bits(bits), dense_pi(d, h), c)
+    check_codes(k, k_ref, T, c, "edge rows", max_frac=2.0 / k.size)
+    assert np.all(k[0] == 7) and np.all(k[4] == 7) and s.cpu()[0] == 0 and s.cpu()[4] == 0
+    one, _ = orbq.rpbh_quantize(dev_bf16(bits[2:3]), rot, cb)
+    assert torch.equal(one.cpu(), codes.cpu()[2:3])
+    # strided input (ldx > d) and padded output (ldy > m)
+    big = np.zeros((5, d + 64), np.uint16)
+    big[:, :d] = bits
+    dbig = dev_bf16(big)
+    c2, _ = orbq.rpbh_quantize(dbig[:, :d], rot, cb)
+    assert torch.equal(c2.cpu(), codes.cpu())
+    wc, wn = orbq.fold_weights(dev_bf16(bits), rot, cb)
+    Yp = torch.full((5, 12), float("nan"), device="cuda")
+    orbq.lut_gemm(codes, s, cb, wc, wn, cb, d, out=Yp[:, :5])
+    assert torch.isnan(Yp[:, 5:]).all() and not torch.isnan(Yp[:, :5]).any()
+    # n = 0 and m = 0 are no-ops
+    e0, s0 = orbq.rpbh_quantize(dev_bf16(bits[:0]), rot, cb)
+    assert e0.numel() == 0

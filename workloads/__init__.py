@@ -184,3 +184,16 @@ def layer_inputs(layer: Layer, rows: int | None = None) -> tuple[np.ndarray, np.
                         layer.outlier_gain)
     w = weights(layer.m, layer.d, layer.w_seed)
     return x, w
+
+
+def random_code_bytes(rows: int, row_bytes: int, seed: int) -> np.ndarray:
+    """Uniformly random packed code bytes [rows, row_bytes] (every byte pattern is a valid
+    packed code array for 2-, 4- and 6-bit codes)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.integers(0, 256, size=(rows, row_bytes), dtype=np.uint8)
+
+
+def random_norms(rows: int, seed: int, lo: float = 0.5, hi: float = 2.0) -> np.ndarray:
+    """Positive per-row scales drawn uniformly from [lo, hi), float64."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    return rng.uniform(lo, hi, rows)
