@@ -1,0 +1,241 @@
+#!/usr/bin/env python3
+"""Benchmark of the OrbitQuant quantized linear layer on one MI355X.
+
+Workload (default): the FLUX MLP-up layer, 4608 tokens x 3072 -> 12288, W4A4, RPBH block 128,
+16-level Lloyd-Max codebooks for f_3072 on both operands; synthetic heavy-tailed activations
+(Student-t(3) x per-channel log-normal scales, 0.1% outlier channels x30) and N(0, 0.02^2)
+weights (workloads.py).  The weights are folded once, untimed (the offline pass).
+
+One step = the whole online hot path on one batch: rpbh_quantize (rotate, normalise, quantize,
+pack the activations) then lut_gemm (decode, MFMA, rescale), both through the C ABI on the
+current stream, inputs already resident in HBM.  The JSON line reports orbq_linear TFLOP/s
+(2 n m d / step time) as `value`, the rpbh_quantize GB/s beside it, the MFMA roofline of the
+dominant kernel (lut_gemm) from HIP events around its launches, and the CPU oracle timed on
+a bounded sample.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+MALL_BYTES = 256 << 20       # Infinity Cache
+
+
+def _sha(path: str) -> str:
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+
+
+def _traffic(kernel_src: str, name: str, workload: str):
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None when the
+    summary is missing or the kernel source changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_{workload}.pmc.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if rec.get("source_sha256") != _sha(kernel_src):
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default=None)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-tokens", type=int, default=1024)
+    ap.add_argument("--cpu-weights", type=int, default=4096)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is data-parallel "
+              "over tokens and the multi-GPU sharding is not built.", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import calibration_free_w4a4_amd as orbq
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    name = args.workload or workloads.HEADLINE
+    L = workloads.CONFIGS[name]
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X_bits, W_bits = workloads.layer_inputs(L)
+    X, W = to_dev(X_bits), to_dev(W_bits)
+    perm, signs = workloads.rotation(L.d)
+    rot = orbq.Rotation.create(L.d, L.block, perm, signs)
+    cb_a = orbq.Codebook.lloyd_max(L.d, L.bits_a)
+    cb_w = orbq.Codebook.lloyd_max(L.d, L.bits_w)
+    w_codes, w_norms = orbq.fold_weights(W, rot, cb_w)           # offline, untimed
+    x_codes = torch.empty((L.n, orbq.codes_row_bytes(L.d, L.bits_a)), dtype=torch.uint8, device=dev)
+    x_norms = torch.empty((L.n,), dtype=torch.float32, device=dev)
+    Y = torch.empty((L.n, L.m), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty((orbq.linear_workspace_bytes(L.n, L.d, L.bits_a),), dtype=torch.uint8, device=dev)
+
+    def quantize(Xin=X):
+        orbq.rpbh_quantize(Xin, rot, cb_a, out_codes=x_codes, out_norms=x_norms)
+
+    def gemm():
+        orbq.lut_gemm(x_codes, x_norms, cb_a, w_codes, w_norms, cb_w, L.d, out=Y)
+
+    for _ in range(args.warmup):
+        quantize()
+        gemm()
+    torch.cuda.synchronize()
+
+    # ---- timed region: K steps, HIP events around each kernel on the launch stream
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        ev[k][0].record()
+        quantize()
+        ev[k][1].record()
+        gemm()
+        ev[k][2].record()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+    q_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
+    g_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in ev)
+
+    flops = L.flops
+    q_bytes = L.n * (2 * L.d + L.d * L.bits_a // 8 + 4)
+    value = flops / (ms_step * 1e-3) / 1e12
+
+    # ---- the same layer through the single orbq_linear entry point (cross-check)
+    for _ in range(3):
+        orbq.linear(X, rot, cb_a, w_codes, w_norms, cb_w, workspace=ws, out=Y)
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        orbq.linear(X, rot, cb_a, w_codes, w_norms, cb_w, workspace=ws, out=Y)
+    torch.cuda.synchronize()
+    linear_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+
+    # ---- rpbh_quantize with inputs rotated over > 2x the 256 MB Infinity Cache
+    nbuf = max(2, -(-2 * MALL_BYTES // (L.n * L.d * 2)))
+    bufs = [X] + [X.roll(k + 1, dims=0).contiguous() for k in range(nbuf - 1)]
+    reps = max(2, args.steps // nbuf) * nbuf
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for b in bufs:
+        quantize(b)
+    torch.cuda.synchronize()
+    e0.record()
+    for k in range(reps):
+        quantize(bufs[k % nbuf])
+    e1.record()
+    torch.cuda.synchronize()
+    q_cold_ms = e0.elapsed_time(e1) / reps
+    del bufs
+
+    # ---- context: torch's bf16 GEMM of the same shape and a same-size copy
+    A = torch.randn((L.n, L.d), dtype=torch.bfloat16, device=dev)
+    B = torch.randn((L.d, L.m), dtype=torch.bfloat16, device=dev)
+    for _ in range(3):
+        torch.matmul(A, B, out=Y)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(20):
+        torch.matmul(A, B, out=Y)
+    e1.record()
+    torch.cuda.synchronize()
+    ref_gemm_tflops = flops / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12
+    src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(10):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 2 * src.numel() / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+    del src, dst, A, B
+
+    gemm_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "lut_gemm.hip")
+    quant_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "rpbh_quantize.hip")
+    g_tflops = flops / (g_ms * 1e-3) / 1e12
+    q_gbps = q_bytes / (q_ms * 1e-3) / 1e9
+    line = {
+        "metric": "orbq_linear TFLOP/s + rpbh_quantize GB/s, FLUX-shaped 4608x3072->12288 W4A4",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "tokens": L.n, "d": L.d, "m": L.m, "bits_w": L.bits_w,
+                   "bits_a": L.bits_a, "block": L.block, "y_dtype": "bf16"},
+        "rpbh_quantize_GBps": round(q_gbps, 1),
+        "rpbh_quantize_cold_GBps": round(q_bytes / (q_cold_ms * 1e-3) / 1e9, 1),
+        "kernel_ms": {"rpbh_quantize": round(q_ms, 5), "lut_gemm": round(g_ms, 5),
+                      "rpbh_quantize_cold": round(q_cold_ms, 5), "orbq_linear_call": round(linear_ms, 5)},
+        "roofline": {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(g_tflops / BF16_PEAK_TFLOPS, 4),
+                     "traffic": _traffic(gemm_src, "lut_gemm", name)},
+        "rpbh_roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
+                          "frac": round(q_gbps / HBM_PEAK_GBPS, 4),
+                          "traffic": _traffic(quant_src, "rpbh_quantize", name)},
+        "context": {"torch_bf16_matmul_TFLOPs": round(ref_gemm_tflops, 1),
+                    "torch_copy_GBps": round(copy_gbps, 1)},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(L, X_bits, W_bits, perm, signs, args.cpu_tokens, args.cpu_weights)
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+def cpu_baseline(L, X_bits, W_bits, perm, signs, n_tok, n_w):
+    """The oracle as it stands (numpy float64) on a bounded sample of the same layer: the
+    first n_tok tokens against the first n_w weight rows (weights folded untimed)."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+
+    import oracle
+    import workloads
+
+    n_tok, n_w = min(n_tok, L.n), min(n_w, L.m)
+    Pi = oracle.rpbh_matrix(L.d, L.block, perm, signs)
+    c_a = oracle.lloyd_max(L.d, L.bits_a).astype(np.float32)
+    c_w = oracle.lloyd_max(L.d, L.bits_w).astype(np.float32)
+    kw, r, _, _ = oracle.fold_weights(workloads.f64_from_bf16_bits(W_bits[:n_w]), Pi, c_w)
+    Xs = workloads.f64_from_bf16_bits(X_bits[:n_tok])
+    t0 = time.perf_counter()
+    oracle.orbq_linear(Xs, Pi, c_a, kw, r, c_w)
+    dt = time.perf_counter() - t0
+    threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
+    return {"value": round(2.0 * n_tok * n_w * L.d / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2),
+            "sample": f"first {n_tok} tokens x first {n_w} weight rows of {L.name} (d={L.d}); "
+                      "rotate + quantize + float64 dequantised product"}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

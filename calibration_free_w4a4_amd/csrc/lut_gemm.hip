@@ -4,12 +4,13 @@
 // W^' = diag(r') Q(W~') ("Offline Weight Quantization"), and W^' x^' approximates W x because the
 // rotation cancels.  The product is a dense contraction over d, so it runs on the matrix cores.
 //
-// Kernel layout (gfx950, wave64, 256 threads):
-//   * workgroup tile 256 tokens x 256 weight rows, K tile of 32; 4 waves, each 128 x 128,
-//     v_mfma_f32_32x32x16_bf16 with fp32 accumulators (16 tiles of 32 x 32 per wave).
-//   * each thread loads one token row and one weight row of the K tile (8..24 bytes of packed
-//     codes), decodes them to bf16 centroid values and stores them to LDS; the MFMA operands
-//     are 16-byte LDS reads.  LDS is double buffered, one barrier per K tile.
+// Kernel layout (gfx950, wave64, 512 threads = 8 waves, two per SIMD):
+//   * workgroup tile 256 tokens x 256 weight rows, K tile of 32; each wave computes 64 x 128
+//     with v_mfma_f32_32x32x16_bf16 and fp32 accumulators (2 x 4 tiles of 32 x 32).
+//   * waves 0-3 load the 256 token code rows of the K tile, waves 4-7 the 256 weight code rows
+//     (8..24 bytes per thread), decode them to bf16 centroid values and store them to LDS; the
+//     MFMA operands are 16-byte LDS reads.  Code rows are prefetched two K tiles ahead in
+//     registers; LDS is double buffered, one barrier per K tile.
 //   * decode of 4-bit codes: v_perm_b32 byte lookups into the 8 bf16 magnitudes (held in four
 //     registers) plus the sign bit; 2-bit codes use a 256-entry LDS table per code byte, 6-bit
 //     codes a 4096-entry LDS table per code pair.  Every decoder writes the 8 values of a
@@ -26,7 +27,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 constexpr int BM = 256, BN = 256, KT = 32;
-constexpr int kThreads = 256;
+constexpr int kThreads = 512;
 
 struct GemmArgs {
   const uint8_t* xc;
@@ -149,138 +150,169 @@ __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
   return static_cast<uint32_t>(row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4));
 }
 
+constexpr size_t lut_bytes_dev(int bits) { return bits == 2 ? 256 * 8 : bits == 6 ? 4096 * 4 : 0; }
+
+template <int BITS>
+__device__ __forceinline__ void build_lut(const uint16_t* mag, unsigned char* p, int tid) {
+  if constexpr (BITS == 2) {
+    uint2* l = reinterpret_cast<uint2*>(p);
+    for (int b = tid; b < 256; b += kThreads) {
+      const uint32_t c0 = mag_signed(mag, b & 3, 2), c1 = mag_signed(mag, (b >> 2) & 3, 2);
+      const uint32_t c2 = mag_signed(mag, (b >> 4) & 3, 2), c3 = mag_signed(mag, (b >> 6) & 3, 2);
+      l[b] = make_uint2(c0 | (c2 << 16), c1 | (c3 << 16));
+    }
+  } else if constexpr (BITS == 6) {
+    uint32_t* l = reinterpret_cast<uint32_t*>(p);
+    for (int i = tid; i < 4096; i += kThreads)
+      l[i] = mag_signed(mag, i & 63, 6) | (static_cast<uint32_t>(mag_signed(mag, i >> 6, 6)) << 16);
+  }
+}
+
 template <int BA, int BW, bool OUT_BF16>
 __global__ __launch_bounds__(kThreads, 1) void k_lut_gemm(GemmArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* As = smem;                  // [2][256][32] bf16
+  unsigned char* As = smem;                    // [2][256][32] bf16
   unsigned char* Bs = smem + 2 * BM * KT * 2;  // [2][256][32] bf16
   unsigned char* lut = Bs + 2 * BN * KT * 2;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave & 3, wn = wave >> 2;     // 64-row band of tokens, 128-row band of weights
 
-  const int tile = blockIdx.x;
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give each XCD a
+  // contiguous band of tiles (neighbouring tiles share code rows in that XCD's L2)
+  const int ntiles = a.tiles_n * a.tiles_m;
+  int tile = blockIdx.x;
+  if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
   const int tn = tile % a.tiles_n, tm = tile / a.tiles_n;
   const int64_t row0 = static_cast<int64_t>(tn) * BM;  // token rows
   const int64_t col0 = static_cast<int64_t>(tm) * BN;  // weight rows
 
-  // decode tables
-  const Tab4 ta{a.lt_lo_a, a.lt_hi_a, a.ht_lo_a, a.ht_hi_a};
-  const Tab4 tw{a.lt_lo_w, a.lt_hi_w, a.ht_lo_w, a.ht_hi_w};
-  void* lut_a = nullptr;
-  void* lut_w = nullptr;
-  {
-    unsigned char* p = lut;
-    auto build = [&](int bits, const uint16_t* mag) -> void* {
-      void* base = p;
-      if (bits == 2) {
-        uint2* l = reinterpret_cast<uint2*>(p);
-        for (int b = tid; b < 256; b += kThreads) {
-          const uint32_t c0 = mag_signed(mag, b & 3, 2), c1 = mag_signed(mag, (b >> 2) & 3, 2);
-          const uint32_t c2 = mag_signed(mag, (b >> 4) & 3, 2), c3 = mag_signed(mag, (b >> 6) & 3, 2);
-          l[b] = make_uint2(c0 | (c2 << 16), c1 | (c3 << 16));
-        }
-        p += 256 * sizeof(uint2);
-      } else if (bits == 6) {
-        uint32_t* l = reinterpret_cast<uint32_t*>(p);
-        for (int i = tid; i < 4096; i += kThreads)
-          l[i] = mag_signed(mag, i & 63, 6) | (static_cast<uint32_t>(mag_signed(mag, i >> 6, 6)) << 16);
-        p += 4096 * sizeof(uint32_t);
-      }
-      return base;
-    };
-    lut_a = build(BA, a.mag_a);
-    lut_w = build(BW, a.mag_w);
+  // decode tables: 2- and 6-bit codes decode through LDS tables built from the magnitudes
+  uint16_t* mags = reinterpret_cast<uint16_t*>(lut);  // [0, 32): activations, [32, 64): weights
+  unsigned char* lut_a = lut + 128;
+  unsigned char* lut_w = lut_a + lut_bytes_dev(BA);
+  if constexpr (BA != 4 || BW != 4) {
+#pragma unroll
+    for (int r = 0; r < 32; ++r) {
+      if (tid == r) mags[r] = a.mag_a[r];
+      if (tid == 32 + r) mags[32 + r] = a.mag_w[r];
+    }
+    __syncthreads();
+    build_lut<BA>(mags, lut_a, tid);
+    build_lut<BW>(mags + 32, lut_w, tid);
   }
 
-  // this thread's global rows (clamped; rows past the end are computed and discarded)
-  const int64_t xr = min(row0 + tid, a.n - 1);
-  const int64_t wr = min(col0 + tid, a.m - 1);
-  const uint8_t* xrow = a.xc + xr * a.xrow_bytes;
-  const uint8_t* wrow = a.wc + wr * a.wrow_bytes;
-
-  RowTile<BA> ra;
-  RowTile<BW> rw;
+  // loader role: threads 0-255 stage token row tid, threads 256-511 weight row tid-256
+  const bool loads_a = tid < BM;
+  const int lrow = loads_a ? tid : tid - BM;
+  const uint8_t* arow = a.xc + min(row0 + lrow, a.n - 1) * a.xrow_bytes;  // rows past the end are
+  const uint8_t* brow = a.wc + min(col0 + lrow, a.m - 1) * a.wrow_bytes;  // computed and discarded
+  const Tab4 ta{a.lt_lo_a, a.lt_hi_a, a.ht_lo_a, a.ht_hi_a};
+  const Tab4 tw{a.lt_lo_w, a.lt_hi_w, a.ht_lo_w, a.ht_hi_w};
   const int nk = static_cast<int>(a.d / KT);
 
-  auto stage = [&](int buf) {
-    uint4 ca[4], cw[4];
-    ra.decode(ca, ta, lut_a);
-    rw.decode(cw, tw, lut_w);
-    unsigned char* at = As + buf * (BM * KT * 2);
-    unsigned char* bt = Bs + buf * (BN * KT * 2);
+  f32x16_t acc[2][4];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      *reinterpret_cast<uint4*>(at + tile_off(tid, c)) = ca[c];
-      *reinterpret_cast<uint4*>(bt + tile_off(tid, c)) = cw[c];
-    }
-  };
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int i = 0; i < 2; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-  ra.load(xrow, 0);
-  rw.load(wrow, 0);
-  __syncthreads();  // decode tables built
-  stage(0);
-  __syncthreads();
-
   const int g = lane >> 5, l32 = lane & 31;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int buf = kt & 1;
-    if (kt + 1 < nk) {
-      ra.load(xrow, kt + 1);
-      rw.load(wrow, kt + 1);
-    }
-    const unsigned char* at = As + buf * (BM * KT * 2);
-    const unsigned char* bt = Bs + buf * (BN * KT * 2);
+  // Fragment addresses: row (band + 32 i + l32), chunk (2 ks + g) xor the row swizzle.  The
+  // swizzle depends only on l32, so per lane two bases (ks = 0, 1) per operand suffice and
+  // the tile index i / j and the buffer become immediate offsets.
+  const uint32_t sw = (l32 >> 1) & 3;
+  const uint32_t a_base = (wm * 64 + l32) * 64, b_base = (wn * 128 + l32) * 64;
+  const uint32_t ch0 = ((0u | g) ^ sw) << 4, ch1 = ((2u | g) ^ sw) << 4;
+  const uint32_t a_off[2] = {a_base + ch0, a_base + ch1};
+  const uint32_t b_off[2] = {b_base + ch0 + 2 * BM * KT * 2, b_base + ch1 + 2 * BM * KT * 2};
+  auto compute = [&](int buf) {
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
-      const int chunk = 2 * ks + g;
-      bf16x8_t fa[4], fb[4];
+      bf16x8_t fa[2], fb[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(at + tile_off(wm * 128 + 32 * i + l32, chunk));
-        fb[i] = *reinterpret_cast<const bf16x8_t*>(bt + tile_off(wn * 128 + 32 * i + l32, chunk));
-      }
+      for (int i = 0; i < 2; ++i)
+        fa[i] = *reinterpret_cast<const bf16x8_t*>(smem + a_off[ks] + buf * (BM * KT * 2) + i * (32 * 64));
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
+      for (int j = 0; j < 4; ++j)
+        fb[j] = *reinterpret_cast<const bf16x8_t*>(smem + b_off[ks] + buf * (BN * KT * 2) + j * (32 * 64));
 #pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
     }
-    if (kt + 1 < nk) stage(buf ^ 1);
+  };
+
+  // Main loop, specialised per loader role (waves 0-3 stage token rows, waves 4-7 weight rows;
+  // both paths hit the same barriers).  Two K tiles are in flight in registers; the loop is
+  // unrolled by two so that each register set keeps fixed registers.
+  auto main_loop = [&](auto& r0, auto& r1, const uint8_t* crow, const Tab4& tab, const void* lutp,
+                       unsigned char* tbase) {
+    auto stage = [&](int buf, const auto& rt) {
+      uint4 cv[4];
+      rt.decode(cv, tab, lutp);
+      unsigned char* t = tbase + buf * (BM * KT * 2);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(t + tile_off(lrow, c)) = cv[c];
+    };
+    r0.load(crow, 0);
+    r1.load(crow, 1);
+    __syncthreads();  // decode tables built
+    stage(0, r0);
     __syncthreads();
+    // d is a multiple of 64, so nk = d / 32 is even and both halves always run
+    for (int kt = 0; kt < nk; kt += 2) {
+      if (kt + 2 < nk) r0.load(crow, kt + 2);
+      compute(0);
+      stage(1, r1);
+      __syncthreads();
+      if (kt + 3 < nk) r1.load(crow, kt + 3);
+      compute(1);
+      if (kt + 2 < nk) stage(0, r0);
+      __syncthreads();
+    }
+  };
+  if (loads_a) {
+    RowTile<BA> r0, r1;
+    main_loop(r0, r1, arow, ta, lut_a, As);
+  } else {
+    RowTile<BW> r0, r1;
+    main_loop(r0, r1, brow, tw, lut_w, Bs);
   }
 
   // epilogue: D[row][col] of a 32x32 tile: col = lane % 32, row = 8*(r/4) + 4*(lane/32) + r%4
+  const bool full = row0 + BM <= a.n && col0 + BN <= a.m;
   float rn[4];
+  int64_t cols[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
-    const int64_t col = col0 + wn * 128 + 32 * j + l32;
-    rn[j] = col < a.m ? __builtin_bit_cast(float, static_cast<uint32_t>(a.wn[col]) << 16) : 0.0f;
+    cols[j] = col0 + wn * 128 + 32 * j + l32;
+    rn[j] = (full || cols[j] < a.m) ? __builtin_bit_cast(float, static_cast<uint32_t>(a.wn[cols[j]]) << 16) : 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
+  for (int i = 0; i < 2; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = row0 + wm * 128 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (row >= a.n) continue;
+      const int64_t row = row0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (!full && row >= a.n) continue;
       const float sr = a.xs[row];
+      if constexpr (OUT_BF16) {
+        uint16_t* yrow = reinterpret_cast<uint16_t*>(a.Y) + row * a.ldy;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int64_t col = col0 + wn * 128 + 32 * j + l32;
-        if (col >= a.m) continue;
-        const float v = acc[i][j][r] * sr * rn[j];
-        if constexpr (OUT_BF16) {
-          uint32_t u = __builtin_bit_cast(uint32_t, v);
+        for (int j = 0; j < 4; ++j) {
+          if (!full && cols[j] >= a.m) continue;
+          uint32_t u = __builtin_bit_cast(uint32_t, acc[i][j][r] * sr * rn[j]);
           u += 0x7fffu + ((u >> 16) & 1u);
-          reinterpret_cast<uint16_t*>(a.Y)[row * a.ldy + col] = static_cast<uint16_t>(u >> 16);
-        } else {
-          reinterpret_cast<float*>(a.Y)[row * a.ldy + col] = v;
+          yrow[cols[j]] = static_cast<uint16_t>(u >> 16);
+        }
+      } else {
+        float* yrow = reinterpret_cast<float*>(a.Y) + row * a.ldy;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          if (!full && cols[j] >= a.m) continue;
+          yrow[cols[j]] = acc[i][j][r] * sr * rn[j];
         }
       }
     }
@@ -347,7 +379,7 @@ int launch_lut_gemm(const uint8_t* x_codes, const float* x_norms, const DecodePa
     a.mag_w[i] = dw.mag[i];
   }
   const int grid = a.tiles_n * a.tiles_m;
-  const size_t lds = 2 * (BM + BN) * KT * 2 + lut_bytes(da.bits) + lut_bytes(dw.bits);
+  const size_t lds = 2 * (BM + BN) * KT * 2 + 128 + lut_bytes(da.bits) + lut_bytes(dw.bits);
   hipError_t e;
   switch (da.bits) {
     case 2: e = launch_ba<2>(dw.bits, y_bf16 != 0, a, grid, lds, stream); break;

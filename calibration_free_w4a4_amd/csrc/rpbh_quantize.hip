@@ -51,21 +51,41 @@ struct QuantKernelArgs {
   QuantParams qp;
 };
 
+__device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
                                          0.0f, false);
 }
 
-// value of `x` in the lane whose index differs in bit 0 (xor 1) or bit 1 (xor 2) within the quad
-template <int XOR>
-__device__ __forceinline__ float quad_xor(float x) {
-  constexpr int ctrl = XOR == 1 ? 0xB1 : 0x4E;  // quad_perm [1,0,3,2] / [2,3,0,1]
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), ctrl, 0xF, 0xF, false));
-}
+// x[i] += sgn * (x[i] in the lane whose index differs in bit 0 / bit 1), for 8 registers, with
+// v_fmac_f32_dpp (one instruction per element).  The leading s_nop 4 covers the VALU-write ->
+// DPP-read and EXEC-write -> DPP hazards for whatever the compiler placed before the block.
+#define ORBQ_DPP_FMAC8(CTRL, X, S)                                                                  \
+  asm("s_nop 4\n"                                                                                 \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      : "+v"((X)[0]), "+v"((X)[1]), "+v"((X)[2]), "+v"((X)[3]), "+v"((X)[4]), "+v"((X)[5]),       \
+        "+v"((X)[6]), "+v"((X)[7])                                                                 \
+      : "v"(S))
 
 __device__ __forceinline__ int floor_neg_to_int(float x) {
   int r;
   asm("v_cvt_flr_i32_f32_e64 %0, -%1" : "=v"(r) : "v"(x));
+  return r;
+}
+
+__device__ __forceinline__ int med3_i32(int x, int lo, int hi) {
+  int r;
+  asm("v_med3_i32 %0, %1, %2, %3" : "=v"(r) : "v"(x), "s"(lo), "v"(hi));
   return r;
 }
 
@@ -104,10 +124,18 @@ __device__ void build_table(const QuantParams& qp, float2* tbl, int tid, int nth
 }
 
 __device__ __forceinline__ uint32_t quantize_one(float tp, const float2* tbl, int J) {
-  int j = floor_neg_to_int(tp);
-  j = min(max(j, -J), J - 1);
+  const int j = med3_i32(floor_neg_to_int(tp), -J, J - 1);
   const float2 e = tbl[j];  // tbl points at bucket 0
   return static_cast<uint32_t>(__builtin_bit_cast(int, e.y)) + (__builtin_fabsf(tp) > e.x ? 1u : 0u);
+}
+
+// Element offset, within a token row in LDS, of post-permutation position p.  Rows are stored
+// in 16-byte chunks of 8 positions; the chunk index is xor-swizzled within groups of 8 chunks
+// so that the 16-byte reads of the compute lanes (4 consecutive chunks per lane) hit distinct
+// banks for any 8 consecutive lanes.
+__device__ __forceinline__ uint32_t lds_pos(uint32_t p) {
+  const uint32_t ch = p >> 3, g = ch >> 3;
+  return (((g << 3) | ((ch & 7) ^ (g & 3))) << 3) | (p & 7);
 }
 
 template <int H, int BITS, QuantMode MODE>
@@ -123,26 +151,47 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
   const int slot = active ? tid / a.lpt : 0;
   const int q = tid - slot * a.lpt;
   const int J = a.qp.J;
+  const int j0 = active ? kE * q : 0;
 
   if (MODE != QuantMode::kRotateOnly) build_table(a.qp, tbl_all, tid, blockDim.x);
   const float2* tbl = tbl_all + J;
 
-  // loop-invariant gather addresses (LDS byte offsets) and sign masks of this lane's positions
-  uint32_t gaddr[kE];
+  // ---- set-up: inverse permutation in LDS, then this lane's scatter addresses
+  uint16_t* inv = xs;
+  if (active && slot == 0) {
+    const int4* pp = reinterpret_cast<const int4*>(a.perm + j0);
+#pragma unroll
+    for (int c = 0; c < kE / 4; ++c) {
+      const int4 p4 = pp[c];
+      const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) inv[min(max(pv[e], 0), d - 1)] = static_cast<uint16_t>(j0 + 4 * c + e);
+    }
+  }
   uint32_t smask[kE / 2];
   {
-    const int j0 = kE * q;
+    const uint4* sp = reinterpret_cast<const uint4*>(a.signs + j0);
+    const uint4 s0 = sp[0], s1 = sp[1];
+    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+#pragma unroll
+    for (int i = 0; i < kE / 2; ++i) {  // int8 signs: byte 2i and 2i+1 of the lane's 32
+      const uint32_t b = sw[i >> 1] >> (16 * (i & 1));
+      smask[i] = ((b & 0x80u) << 8) | ((b & 0x8000u) << 16);
+    }
+  }
+  __syncthreads();
+  uint32_t saddr[kE];  // LDS byte address of each staged input position after permutation
+  {
     const uint32_t rowbase = static_cast<uint32_t>(slot * d);
 #pragma unroll
-    for (int i = 0; i < kE; ++i) {
-      int p = active ? a.perm[j0 + i] : 0;
-      p = min(max(p, 0), d - 1);
-      gaddr[i] = (rowbase + static_cast<uint32_t>(p)) * 2u;
-    }
+    for (int c = 0; c < 4; ++c) {
+      const uint4 iv = *reinterpret_cast<const uint4*>(inv + 8 * (q + c * a.lpt));
+      const uint32_t w[4] = {iv.x, iv.y, iv.z, iv.w};
 #pragma unroll
-    for (int i = 0; i < kE / 2; ++i) {
-      const int s0 = active ? a.signs[j0 + 2 * i] : 1, s1 = active ? a.signs[j0 + 2 * i + 1] : 1;
-      smask[i] = (s0 < 0 ? 0x8000u : 0u) | (s1 < 0 ? 0x80000000u : 0u);
+      for (int e = 0; e < 8; ++e) {
+        const uint32_t p = min((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, static_cast<uint32_t>(d - 1));
+        saddr[8 * c + e] = (rowbase + lds_pos(p)) * 2u;
+      }
     }
   }
   // cross-lane butterflies leave the result negated in lanes with an odd number of "upper"
@@ -151,51 +200,61 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
   const float lane_sign = (__builtin_popcount(q & (LPB - 1)) & 1) ? -1.0f : 1.0f;
   const float sgn1 = (q & 1) ? -1.0f : 1.0f;
   const float sgn2 = (q & 2) ? -1.0f : 1.0f;
-  constexpr uint32_t kOnes = 0x3F803F80u;     // bf16 (1, 1)
+  constexpr uint32_t kOnes = 0x3F803F80u;      // bf16 (1, 1)
   constexpr uint32_t kPlusMinus = 0xBF803F80u; // bf16 (1, -1)
+  // this lane's 4 compute chunks (positions 32q .. 32q+31) in the swizzled row
+  uint32_t raddr[4];
+#pragma unroll
+  for (int c = 0; c < 4; ++c) raddr[c] = (static_cast<uint32_t>(slot * d) + lds_pos(kE * q + 8 * c)) * 2u;
 
+  // rows past the end (and idle lanes) load a valid row and store nothing
+  auto load_group = [&](int g, uint4 v[4]) {
+    const int64_t row = min(static_cast<int64_t>(g) * a.tg + slot, a.n - 1);
+    const uint16_t* src = a.X + row * a.ldx;
+    const int qq = active ? q : 0;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const uint4*>(src + 8 * (qq + c * a.lpt));
+  };
+
+  uint4 v[4];
+  load_group(blockIdx.x, v);
   for (int g = blockIdx.x; g < a.ngroups; g += gridDim.x) {
     const int64_t row = static_cast<int64_t>(g) * a.tg + slot;
     const bool valid = active && row < a.n;
 
-    // ---- stage 32 input positions of this lane's token into LDS; partial sum of squares
-    uint4 v[4];
-    if (valid) {
-      const uint4* src = reinterpret_cast<const uint4*>(a.X + row * a.ldx + kE * q);
-#pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = src[c];
-    } else {
-#pragma unroll
-      for (int c = 0; c < 4; ++c) v[c] = make_uint4(0, 0, 0, 0);
-    }
-    __syncthreads();  // previous iteration's gathers are done with xs
+    __syncthreads();  // the previous group's reads of xs (and the set-up's reads of inv) are done
+    // ---- scatter the 32 staged positions to their permuted places; partial sum of squares
     float ss = 0.0f;
     if (active) {
-      uint4* dst = reinterpret_cast<uint4*>(xs + slot * d + kE * q);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        dst[c] = v[c];
-        ss += dot2_bf16(v[c].x, v[c].x);
-        ss += dot2_bf16(v[c].y, v[c].y);
-        ss += dot2_bf16(v[c].z, v[c].z);
-        ss += dot2_bf16(v[c].w, v[c].w);
+        const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          *reinterpret_cast<uint16_t*>(smem + saddr[8 * c + 2 * k]) = static_cast<uint16_t>(w[k]);
+          *reinterpret_cast<uint16_t*>(smem + saddr[8 * c + 2 * k + 1]) = static_cast<uint16_t>(w[k] >> 16);
+          ss = dot2_acc(w[k], w[k], ss);
+        }
       }
     }
+    if (g + static_cast<int>(gridDim.x) < a.ngroups) load_group(g + gridDim.x, v);  // prefetch
     for (int off = 1; off < a.seg; off <<= 1) ss += __shfl_xor(ss, off, 64);
     if (active && (q & (a.seg - 1)) == 0) part[slot * a.nseg + q / a.seg] = ss;
     __syncthreads();
     if (!active) continue;
 
-    // ---- gather the permuted positions, apply signs, FWHT stage 1 (+ widening to fp32)
+    // ---- this lane's 32 permuted positions, signs, FWHT stage 1 (+ widening to fp32)
     float y[kE];
 #pragma unroll
-    for (int i = 0; i < kE / 2; ++i) {
-      u16x2_t pr;
-      pr.x = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i]);
-      pr.y = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i + 1]);
-      const uint32_t w = __builtin_bit_cast(uint32_t, pr) ^ smask[i];
-      y[2 * i] = dot2_bf16(w, kOnes);
-      y[2 * i + 1] = dot2_bf16(w, kPlusMinus);
+    for (int c = 0; c < 4; ++c) {
+      const uint4 r4 = *reinterpret_cast<const uint4*>(smem + raddr[c]);
+      const uint32_t w[4] = {r4.x, r4.y, r4.z, r4.w};
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t x2 = w[k] ^ smask[4 * c + k];
+        y[8 * c + 2 * k] = dot2_bf16(x2, kOnes);
+        y[8 * c + 2 * k + 1] = dot2_bf16(x2, kPlusMinus);
+      }
     }
     // ---- FWHT stages 2..5 in registers
 #pragma unroll
@@ -210,12 +269,16 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
     }
     // ---- remaining stages across the lanes of the block: x += sgn * partner
     if constexpr (LPB >= 2) {
-#pragma unroll
-      for (int i = 0; i < kE; ++i) y[i] = __builtin_fmaf(quad_xor<1>(y[i]), sgn1, y[i]);
+      ORBQ_DPP_FMAC8("quad_perm:[1,0,3,2]", y, sgn1);
+      ORBQ_DPP_FMAC8("quad_perm:[1,0,3,2]", y + 8, sgn1);
+      ORBQ_DPP_FMAC8("quad_perm:[1,0,3,2]", y + 16, sgn1);
+      ORBQ_DPP_FMAC8("quad_perm:[1,0,3,2]", y + 24, sgn1);
     }
     if constexpr (LPB >= 4) {
-#pragma unroll
-      for (int i = 0; i < kE; ++i) y[i] = __builtin_fmaf(quad_xor<2>(y[i]), sgn2, y[i]);
+      ORBQ_DPP_FMAC8("quad_perm:[2,3,0,1]", y, sgn2);
+      ORBQ_DPP_FMAC8("quad_perm:[2,3,0,1]", y + 8, sgn2);
+      ORBQ_DPP_FMAC8("quad_perm:[2,3,0,1]", y + 16, sgn2);
+      ORBQ_DPP_FMAC8("quad_perm:[2,3,0,1]", y + 24, sgn2);
     }
 
     // ---- token norm: the lane segments' partial sums, added in a fixed order
@@ -233,24 +296,24 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
       if (q == 0) reinterpret_cast<float*>(a.norms)[row] = s;
       continue;
     } else {
-      const float inv = lane_sign * (a.inv_scale / (s + a.eps));
+      const float inv_s = lane_sign * (a.inv_scale / (s + a.eps));
       if (!valid) continue;
       uint8_t* crow = a.codes + row * static_cast<int64_t>(d * BITS / 8) + q * (kE * BITS / 8);
       if constexpr (BITS == 4) {
         uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
-        for (int i = 0; i < kE; ++i) w[i >> 3] |= quantize_one(y[i] * inv, tbl, J) << (4 * (i & 7));
+        for (int i = 0; i < kE; ++i) w[i >> 3] |= quantize_one(y[i] * inv_s, tbl, J) << (4 * (i & 7));
         *reinterpret_cast<uint4*>(crow) = make_uint4(w[0], w[1], w[2], w[3]);
       } else if constexpr (BITS == 2) {
         uint32_t w[2] = {0, 0};
 #pragma unroll
-        for (int i = 0; i < kE; ++i) w[i >> 4] |= quantize_one(y[i] * inv, tbl, J) << (2 * (i & 15));
+        for (int i = 0; i < kE; ++i) w[i >> 4] |= quantize_one(y[i] * inv_s, tbl, J) << (2 * (i & 15));
         *reinterpret_cast<uint2*>(crow) = make_uint2(w[0], w[1]);
       } else {
         uint32_t w[6] = {0, 0, 0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < kE; ++i) {
-          const uint32_t c = quantize_one(y[i] * inv, tbl, J);
+          const uint32_t c = quantize_one(y[i] * inv_s, tbl, J);
           const int bit = 6 * i, wi = bit >> 5, sh = bit & 31;
           w[wi] |= c << sh;
           if (sh > 26) w[wi + 1] |= c >> (32 - sh);
