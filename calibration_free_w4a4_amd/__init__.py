@@ -30,7 +30,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 
 
 def library_path() -> str:
-    return os.path.join(_HERE, "liborbq.so")
+    """The in-tree liborbq.so, or the file named by the ORBQ_LIBRARY environment variable."""
+    return os.environ.get("ORBQ_LIBRARY") or os.path.join(_HERE, "liborbq.so")
 
 
 class OrbqError(RuntimeError):

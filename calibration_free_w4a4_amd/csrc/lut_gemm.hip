@@ -144,10 +144,14 @@ struct RowTile<6> {
   }
 };
 
-// byte offset of (row, chunk) in a [256][32] bf16 tile; chunks of 16 bytes are xor-swizzled so
-// that the 16-byte reads of 8 consecutive rows hit distinct LDS banks
+// Row swizzle of the 16-byte chunks of a [256][32] bf16 tile (64-byte rows): chunk c of row r
+// sits at c ^ swz(r).  swz takes distinct values on rows {r, r+2, r+4, r+6} and on rows
+// {r, r+4, r+8, r+12}, so 16-byte accesses of any 8 (or 16) consecutive rows at one chunk hit
+// distinct banks whether the LDS serves 128 or 256 bytes per clock.
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) + (r >> 3)) & 3; }
+
 __device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return static_cast<uint32_t>(row * 64 + ((chunk ^ ((row >> 1) & 3)) << 4));
+  return static_cast<uint32_t>(row * 64 + ((chunk ^ swz(row)) << 4));
 }
 
 constexpr size_t lut_bytes_dev(int bits) { return bits == 2 ? 256 * 8 : bits == 6 ? 4096 * 4 : 0; }
@@ -222,7 +226,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_lut_gemm(GemmArgs a) {
   // Fragment addresses: row (band + 32 i + l32), chunk (2 ks + g) xor the row swizzle.  The
   // swizzle depends only on l32, so per lane two bases (ks = 0, 1) per operand suffice and
   // the tile index i / j and the buffer become immediate offsets.
-  const uint32_t sw = (l32 >> 1) & 3;
+  const uint32_t sw = swz(l32);  // the band offsets are multiples of 32 rows: swz(band + l32) = swz(l32)
   const uint32_t a_base = (wm * 64 + l32) * 64, b_base = (wn * 128 + l32) * 64;
   const uint32_t ch0 = ((0u | g) ^ sw) << 4, ch1 = ((2u | g) ^ sw) << 4;
   const uint32_t a_off[2] = {a_base + ch0, a_base + ch1};
@@ -262,15 +266,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_lut_gemm(GemmArgs a) {
     __syncthreads();  // decode tables built
     stage(0, r0);
     __syncthreads();
-    // d is a multiple of 64, so nk = d / 32 is even and both halves always run
+    // d is a multiple of 64, so nk = d / 32 is even and both halves always run.  The loads and
+    // stages are unconditional (tile indices clamped; the extra stage at the end writes a buffer
+    // nobody reads again) so that the compiler can count outstanding loads exactly and waits only
+    // for the tile it decodes, not for the one just issued.
     for (int kt = 0; kt < nk; kt += 2) {
-      if (kt + 2 < nk) r0.load(crow, kt + 2);
+      r0.load(crow, min(kt + 2, nk - 1));
       compute(0);
       stage(1, r1);
       __syncthreads();
-      if (kt + 3 < nk) r1.load(crow, kt + 3);
+      r1.load(crow, min(kt + 3, nk - 1));
       compute(1);
-      if (kt + 2 < nk) stage(0, r0);
+      stage(0, r0);
       __syncthreads();
     }
   };

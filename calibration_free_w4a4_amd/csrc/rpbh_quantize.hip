@@ -8,18 +8,23 @@
 //
 // Work layout (gfx950, wave64):
 //   * 32 consecutive post-permutation positions of one token per lane; a Hadamard block of
-//     h = 128 spans one quad of lanes (h = 64: a lane pair).  A workgroup holds `tg` tokens.
-//   * Each lane loads 32 consecutive input positions of its token (4 x 16-byte loads,
-//     coalesced across the lane's token), stores them to LDS and adds their squares into a
-//     partial norm (sum of squares is invariant under Pi).
-//   * After a barrier each lane gathers its 32 permuted positions from LDS with 16-bit
-//     reads, flips the Rademacher signs with one xor per bf16 pair, and runs the block FWHT:
-//     the first butterfly stage and the bf16 -> fp32 widening together with v_dot2_f32_bf16,
-//     the next four stages in registers, the last log2(h/32) stages across lanes with DPP.
+//     h = 128 spans one quad of lanes (h = 64: a lane pair).  A workgroup holds `tg` tokens and
+//     loops over token groups (persistent grid).
+//   * Staging: the lanes of a token load its bf16 row with coalesced 16-byte loads (lane q takes
+//     chunks q, q + L, q + 2L, q + 3L), prefetched one token group ahead in registers, store it
+//     to LDS and add the squares into a partial norm (sum of squares is invariant under Pi).
+//   * Compute: each lane gathers its 32 permuted positions x[perm[j]] from LDS with 16-bit reads
+//     (addresses precomputed once from perm), flips the Rademacher signs with one xor per bf16
+//     pair, and runs the block FWHT: the first butterfly stage and the bf16 -> fp32 widening
+//     with v_dot2_f32_bf16, the next four stages in registers, the last log2(h/32) stages across
+//     lanes with v_fmac_f32_dpp.
 //   * Quantization uses the power-of-two-scaled coordinate t' = t * 2^k: one table lookup on
 //     floor(-t') and one fp32 compare give the exact nearest-centroid decision (QuantParams).
 //   * Codes are packed in registers and written with one 8/16/24-byte store per lane.
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
 
 #include "internal.h"
 
@@ -48,8 +53,14 @@ struct QuantKernelArgs {
   int32_t ngroups;
   float eps;
   float inv_scale; // 2^k / sqrt(h) (quantize) or 1 / sqrt(h) (rotate only)
+  uint32_t codes_bytes, norms_bytes, rot_bytes;  // buffer extents (< 2^31) for bounds-dropped stores
   QuantParams qp;
 };
+
+typedef int v4i_t __attribute__((ext_vector_type(4)));
+typedef uint32_t v2u_t __attribute__((ext_vector_type(2)));
+constexpr uint32_t kBufWord3 = 0x00020000u;  // raw (untyped) buffer resource, gfx9 family
+constexpr uint32_t kDropped = 0xFFFFFF00u;   // offset past every extent: the store is discarded
 
 __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -129,13 +140,12 @@ __device__ __forceinline__ uint32_t quantize_one(float tp, const float2* tbl, in
   return static_cast<uint32_t>(__builtin_bit_cast(int, e.y)) + (__builtin_fabsf(tp) > e.x ? 1u : 0u);
 }
 
-// Element offset, within a token row in LDS, of post-permutation position p.  Rows are stored
-// in 16-byte chunks of 8 positions; the chunk index is xor-swizzled within groups of 8 chunks
-// so that the 16-byte reads of the compute lanes (4 consecutive chunks per lane) hit distinct
-// banks for any 8 consecutive lanes.
-__device__ __forceinline__ uint32_t lds_pos(uint32_t p) {
-  const uint32_t ch = p >> 3, g = ch >> 3;
-  return (((g << 3) | ((ch & 7) ^ (g & 3))) << 3) | (p & 7);
+
+// bf16 pair dot product with a zero accumulator (VOP3P form, inline constant 0)
+__device__ __forceinline__ float dot2_zero(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "s"(b));
+  return r;
 }
 
 template <int H, int BITS, QuantMode MODE>
@@ -149,49 +159,44 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
   const int nact = a.tg * a.lpt;
   const bool active = tid < nact;
   const int slot = active ? tid / a.lpt : 0;
-  const int q = tid - slot * a.lpt;
+  const int q = active ? tid - slot * a.lpt : 0;
   const int J = a.qp.J;
-  const int j0 = active ? kE * q : 0;
+  const int j0 = kE * q;
+
+  // rows past the end (and idle lanes) load a valid row and store nothing
+  auto load_group = [&](int g, uint4 v[4]) {
+    const int64_t row = min(static_cast<int64_t>(g) * a.tg + slot, a.n - 1);
+    const uint16_t* src = a.X + row * a.ldx;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const uint4*>(src + 8 * (q + c * a.lpt));
+  };
+  uint4 v[4];
+  load_group(blockIdx.x, v);  // first group in flight during the set-up
 
   if (MODE != QuantMode::kRotateOnly) build_table(a.qp, tbl_all, tid, blockDim.x);
   const float2* tbl = tbl_all + J;
 
-  // ---- set-up: inverse permutation in LDS, then this lane's scatter addresses
-  uint16_t* inv = xs;
-  if (active && slot == 0) {
+  // ---- set-up: gather addresses x[perm[j]] (LDS byte offsets) and sign masks of this lane
+  uint32_t gaddr[kE];
+  uint32_t smask[kE / 2];
+  {
     const int4* pp = reinterpret_cast<const int4*>(a.perm + j0);
+    const uint32_t rowbase = static_cast<uint32_t>(slot * d);
 #pragma unroll
     for (int c = 0; c < kE / 4; ++c) {
       const int4 p4 = pp[c];
       const int pv[4] = {p4.x, p4.y, p4.z, p4.w};
 #pragma unroll
-      for (int e = 0; e < 4; ++e) inv[min(max(pv[e], 0), d - 1)] = static_cast<uint16_t>(j0 + 4 * c + e);
+      for (int e = 0; e < 4; ++e)
+        gaddr[4 * c + e] = (rowbase + static_cast<uint32_t>(min(max(pv[e], 0), d - 1))) * 2u;
     }
-  }
-  uint32_t smask[kE / 2];
-  {
     const uint4* sp = reinterpret_cast<const uint4*>(a.signs + j0);
     const uint4 s0 = sp[0], s1 = sp[1];
     const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-    for (int i = 0; i < kE / 2; ++i) {  // int8 signs: byte 2i and 2i+1 of the lane's 32
+    for (int i = 0; i < kE / 2; ++i) {  // int8 signs 2i, 2i+1 -> sign bits of a bf16 pair
       const uint32_t b = sw[i >> 1] >> (16 * (i & 1));
       smask[i] = ((b & 0x80u) << 8) | ((b & 0x8000u) << 16);
-    }
-  }
-  __syncthreads();
-  uint32_t saddr[kE];  // LDS byte address of each staged input position after permutation
-  {
-    const uint32_t rowbase = static_cast<uint32_t>(slot * d);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 iv = *reinterpret_cast<const uint4*>(inv + 8 * (q + c * a.lpt));
-      const uint32_t w[4] = {iv.x, iv.y, iv.z, iv.w};
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const uint32_t p = min((w[e >> 1] >> (16 * (e & 1))) & 0xFFFFu, static_cast<uint32_t>(d - 1));
-        saddr[8 * c + e] = (rowbase + lds_pos(p)) * 2u;
-      }
     }
   }
   // cross-lane butterflies leave the result negated in lanes with an odd number of "upper"
@@ -202,59 +207,52 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
   const float sgn2 = (q & 2) ? -1.0f : 1.0f;
   constexpr uint32_t kOnes = 0x3F803F80u;      // bf16 (1, 1)
   constexpr uint32_t kPlusMinus = 0xBF803F80u; // bf16 (1, -1)
-  // this lane's 4 compute chunks (positions 32q .. 32q+31) in the swizzled row
-  uint32_t raddr[4];
+  uint4* stage_dst[4];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) raddr[c] = (static_cast<uint32_t>(slot * d) + lds_pos(kE * q + 8 * c)) * 2u;
+  for (int c = 0; c < 4; ++c) stage_dst[c] = reinterpret_cast<uint4*>(xs + slot * d + 8 * (q + c * a.lpt));
 
-  // rows past the end (and idle lanes) load a valid row and store nothing
-  auto load_group = [&](int g, uint4 v[4]) {
-    const int64_t row = min(static_cast<int64_t>(g) * a.tg + slot, a.n - 1);
-    const uint16_t* src = a.X + row * a.ldx;
-    const int qq = active ? q : 0;
-#pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const uint4*>(src + 8 * (qq + c * a.lpt));
-  };
+  // Stores go through buffer resources: lanes with nothing to store (rows past the end, idle
+  // lanes) get an offset past the extent and the hardware drops the store.  The loop body has no
+  // branches around memory operations, so the compiler's wait counts stay exact (on gfx9 vmcnt
+  // also counts stores: a conservative wait would stall on the previous group's stores).
+  const __amdgpu_buffer_rsrc_t codes_rs = __builtin_amdgcn_make_buffer_rsrc(a.codes, 0, a.codes_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t norms_rs = __builtin_amdgcn_make_buffer_rsrc(a.norms, 0, a.norms_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t rot_rs = __builtin_amdgcn_make_buffer_rsrc(a.x_rot, 0, a.rot_bytes, kBufWord3);
+  const uint32_t row_bytes = static_cast<uint32_t>(d * BITS / 8);
 
-  uint4 v[4];
-  load_group(blockIdx.x, v);
   for (int g = blockIdx.x; g < a.ngroups; g += gridDim.x) {
     const int64_t row = static_cast<int64_t>(g) * a.tg + slot;
     const bool valid = active && row < a.n;
 
-    __syncthreads();  // the previous group's reads of xs (and the set-up's reads of inv) are done
-    // ---- scatter the 32 staged positions to their permuted places; partial sum of squares
+    __syncthreads();  // the previous group's gathers from xs are done
+    // ---- stage this lane's 4 chunks; partial sum of squares
     float ss = 0.0f;
     if (active) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t w[4] = {v[c].x, v[c].y, v[c].z, v[c].w};
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          *reinterpret_cast<uint16_t*>(smem + saddr[8 * c + 2 * k]) = static_cast<uint16_t>(w[k]);
-          *reinterpret_cast<uint16_t*>(smem + saddr[8 * c + 2 * k + 1]) = static_cast<uint16_t>(w[k] >> 16);
-          ss = dot2_acc(w[k], w[k], ss);
-        }
-      }
+      for (int c = 0; c < 4; ++c) *stage_dst[c] = v[c];
     }
-    if (g + static_cast<int>(gridDim.x) < a.ngroups) load_group(g + gridDim.x, v);  // prefetch
+#pragma unroll
+    for (int c = 0; c < 4; ++c) {
+      ss = dot2_acc(v[c].x, v[c].x, ss);
+      ss = dot2_acc(v[c].y, v[c].y, ss);
+      ss = dot2_acc(v[c].z, v[c].z, ss);
+      ss = dot2_acc(v[c].w, v[c].w, ss);
+    }
+    // prefetch the next group (the last iteration reloads its own group: no branch)
+    load_group(g + static_cast<int>(gridDim.x) < a.ngroups ? g + static_cast<int>(gridDim.x) : g, v);
     for (int off = 1; off < a.seg; off <<= 1) ss += __shfl_xor(ss, off, 64);
     if (active && (q & (a.seg - 1)) == 0) part[slot * a.nseg + q / a.seg] = ss;
     __syncthreads();
-    if (!active) continue;
 
-    // ---- this lane's 32 permuted positions, signs, FWHT stage 1 (+ widening to fp32)
+    // ---- gather the 32 permuted positions as bf16 pairs, signs, FWHT stage 1 (+ widening)
     float y[kE];
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
-      const uint4 r4 = *reinterpret_cast<const uint4*>(smem + raddr[c]);
-      const uint32_t w[4] = {r4.x, r4.y, r4.z, r4.w};
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const uint32_t x2 = w[k] ^ smask[4 * c + k];
-        y[8 * c + 2 * k] = dot2_bf16(x2, kOnes);
-        y[8 * c + 2 * k + 1] = dot2_bf16(x2, kPlusMinus);
-      }
+    for (int i = 0; i < kE / 2; ++i) {
+      const uint32_t lo = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i]);
+      const uint32_t hi = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i + 1]);
+      const uint32_t x2 = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ smask[i];
+      y[2 * i] = dot2_zero(x2, kOnes);
+      y[2 * i + 1] = dot2_zero(x2, kPlusMinus);
     }
     // ---- FWHT stages 2..5 in registers
 #pragma unroll
@@ -285,30 +283,34 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
     float s2 = 0.0f;
     for (int k = 0; k < a.nseg; ++k) s2 += part[slot * a.nseg + k];
     const float s = __builtin_sqrtf(s2);
+    const uint32_t lane_row = static_cast<uint32_t>(row);  // < n < 2^31 within a launch chunk
 
     if constexpr (MODE == QuantMode::kRotateOnly) {
-      if (!valid) continue;
       const float sc = a.inv_scale * lane_sign;
-      float4* dst = reinterpret_cast<float4*>(a.x_rot + row * d + kE * q);
+      const uint32_t off = valid ? (lane_row * static_cast<uint32_t>(d) + kE * q) * 4u : kDropped;
 #pragma unroll
-      for (int c = 0; c < kE / 4; ++c)
-        dst[c] = make_float4(y[4 * c] * sc, y[4 * c + 1] * sc, y[4 * c + 2] * sc, y[4 * c + 3] * sc);
-      if (q == 0) reinterpret_cast<float*>(a.norms)[row] = s;
-      continue;
+      for (int c = 0; c < kE / 4; ++c) {
+        const v4i_t w = {__builtin_bit_cast(int, y[4 * c] * sc), __builtin_bit_cast(int, y[4 * c + 1] * sc),
+                         __builtin_bit_cast(int, y[4 * c + 2] * sc), __builtin_bit_cast(int, y[4 * c + 3] * sc)};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rot_rs, off + 16u * c, 0, 0);
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, s), norms_rs,
+                                            (valid && q == 0) ? lane_row * 4u : kDropped, 0, 0);
     } else {
       const float inv_s = lane_sign * (a.inv_scale / (s + a.eps));
-      if (!valid) continue;
-      uint8_t* crow = a.codes + row * static_cast<int64_t>(d * BITS / 8) + q * (kE * BITS / 8);
+      const uint32_t off = valid ? lane_row * row_bytes + q * (kE * BITS / 8) : kDropped;
       if constexpr (BITS == 4) {
         uint32_t w[4] = {0, 0, 0, 0};
 #pragma unroll
         for (int i = 0; i < kE; ++i) w[i >> 3] |= quantize_one(y[i] * inv_s, tbl, J) << (4 * (i & 7));
-        *reinterpret_cast<uint4*>(crow) = make_uint4(w[0], w[1], w[2], w[3]);
+        const v4i_t wv = {static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]), static_cast<int>(w[3])};
+        __builtin_amdgcn_raw_buffer_store_b128(wv, codes_rs, off, 0, 0);
       } else if constexpr (BITS == 2) {
         uint32_t w[2] = {0, 0};
 #pragma unroll
         for (int i = 0; i < kE; ++i) w[i >> 4] |= quantize_one(y[i] * inv_s, tbl, J) << (2 * (i & 15));
-        *reinterpret_cast<uint2*>(crow) = make_uint2(w[0], w[1]);
+        const v2u_t wv = {w[0], w[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(wv, codes_rs, off, 0, 0);
       } else {
         uint32_t w[6] = {0, 0, 0, 0, 0, 0};
 #pragma unroll
@@ -318,17 +320,17 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
           w[wi] |= c << sh;
           if (sh > 26) w[wi + 1] |= c >> (32 - sh);
         }
-        uint2* dst = reinterpret_cast<uint2*>(crow);
-        dst[0] = make_uint2(w[0], w[1]);
-        dst[1] = make_uint2(w[2], w[3]);
-        dst[2] = make_uint2(w[4], w[5]);
+        const v2u_t w0 = {w[0], w[1]}, w1 = {w[2], w[3]}, w2 = {w[4], w[5]};
+        __builtin_amdgcn_raw_buffer_store_b64(w0, codes_rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(w1, codes_rs, off + 8u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b64(w2, codes_rs, off + 16u, 0, 0);
       }
-      if (q == 0) {
-        if constexpr (MODE == QuantMode::kWeights)
-          reinterpret_cast<uint16_t*>(a.norms)[row] = bf16_rne_dev(s);
-        else
-          reinterpret_cast<float*>(a.norms)[row] = s;
-      }
+      if constexpr (MODE == QuantMode::kWeights)
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(bf16_rne_dev(s)), norms_rs,
+                                              (valid && q == 0) ? lane_row * 2u : kDropped, 0, 0);
+      else
+        __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, s), norms_rs,
+                                              (valid && q == 0) ? lane_row * 4u : kDropped, 0, 0);
     }
   }
 }
@@ -418,28 +420,47 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
   while (seg < 64 && (a.lpt % (seg * 2)) == 0) seg *= 2;
   a.seg = seg;
   a.nseg = a.lpt / seg;
-  a.ngroups = static_cast<int>((n + a.tg - 1) / a.tg);
   const float rsqrt_h = 1.0f / __builtin_sqrtf(static_cast<float>(rot.block));
   a.inv_scale = (mode == QuantMode::kRotateOnly) ? rsqrt_h : static_cast<float>(static_cast<double>(a.qp.scale) /
                                                                                  std::sqrt(static_cast<double>(rot.block)));
   const size_t lds = ((static_cast<size_t>(a.tg) * rot.d * 2 + 15) & ~size_t(15)) +
                      sizeof(float2) * 2 * a.qp.J + sizeof(float) * a.tg * a.nseg;
-  // balanced persistent grid: every workgroup runs the same number of token groups
-  const int max_grid = device_cu_count() * 8;
-  const int iters = (a.ngroups + max_grid - 1) / max_grid;
-  const int grid = (a.ngroups + iters - 1) / iters;
-  hipError_t e;
+  // rows per launch: every buffer extent (codes, norms, rotated rows) stays below 2^31 bytes
+  const int64_t bytes_per_row = std::max<int64_t>(rot.d * 4, rot.d);
+  const int64_t chunk_rows = std::max<int64_t>(a.tg, ((int64_t(1) << 31) - 4096) / bytes_per_row / a.tg * a.tg);
+  hipError_t e = hipSuccess;
   const int bits = a.qp.bits;
-  switch (mode) {
-    case QuantMode::kActivations:
-      e = launch_mode<QuantMode::kActivations>(rot.block, bits, a, best_threads, lds, grid, stream);
-      break;
-    case QuantMode::kWeights:
-      e = launch_mode<QuantMode::kWeights>(rot.block, bits, a, best_threads, lds, grid, stream);
-      break;
-    default:
-      e = launch_mode<QuantMode::kRotateOnly>(rot.block, 4, a, best_threads, lds, grid, stream);
-      break;
+  for (int64_t r0 = 0; r0 < n && e == hipSuccess; r0 += chunk_rows) {
+    QuantKernelArgs c = a;
+    const int64_t rows = std::min<int64_t>(chunk_rows, n - r0);
+    c.n = rows;
+    c.X = X + r0 * ldx;
+    const int64_t cb = static_cast<int64_t>(rot.d) * (mode == QuantMode::kRotateOnly ? 4 : a.qp.bits) / 8;
+    if (codes) c.codes = codes + r0 * cb;
+    c.codes_bytes = static_cast<uint32_t>(rows * cb);
+    const int64_t nb = mode == QuantMode::kWeights ? 2 : 4;
+    c.norms = static_cast<unsigned char*>(norms) + r0 * nb;
+    c.norms_bytes = static_cast<uint32_t>(rows * nb);
+    if (x_rot) c.x_rot = x_rot + r0 * rot.d;
+    c.rot_bytes = x_rot ? static_cast<uint32_t>(rows * rot.d * 4) : 0u;
+    c.ngroups = static_cast<int>((rows + a.tg - 1) / a.tg);
+    // balanced persistent grid: every workgroup runs the same number of token groups, and all of
+    // them fit on the chip at once (4 waves per SIMD at <= 128 VGPRs)
+    const int waves_per_wg = best_threads / 64;
+    const int max_grid = device_cu_count() * std::max(1, 16 / waves_per_wg);
+    const int iters = (c.ngroups + max_grid - 1) / max_grid;
+    const int grid = (c.ngroups + iters - 1) / iters;
+    switch (mode) {
+      case QuantMode::kActivations:
+        e = launch_mode<QuantMode::kActivations>(rot.block, bits, c, best_threads, lds, grid, stream);
+        break;
+      case QuantMode::kWeights:
+        e = launch_mode<QuantMode::kWeights>(rot.block, bits, c, best_threads, lds, grid, stream);
+        break;
+      default:
+        e = launch_mode<QuantMode::kRotateOnly>(rot.block, 4, c, best_threads, lds, grid, stream);
+        break;
+    }
   }
   return static_cast<int>(e);
 }
