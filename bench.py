@@ -31,6 +31,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBPS = 8000.0       # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
 MALL_BYTES = 256 << 20       # Infinity Cache
+SETTLE_S = 1.0               # untimed steady-state work before the warmup steps
+CPU_SECONDS = 10.0           # the oracle's CPU leg repeats its sample until this much time
 
 
 def _sha(path: str) -> str:
@@ -38,15 +40,39 @@ def _sha(path: str) -> str:
 
 
 def _traffic(kernel_src: str, name: str, workload: str):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary, or None when the
-    summary is missing or the kernel source changed since the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{name}_{workload}.pmc.json")
+    """HBM bytes per launch from a committed rocprofv3 --pmc summary (profiles/, lines of
+    `key: value`), or None when the summary is missing or the kernel source changed since
+    the counters were taken."""
+    path = os.path.join(ROOT, "profiles", f"{name}_{workload}.pmc.txt")
     if not os.path.exists(path):
         return None
-    rec = json.load(open(path))
+    rec = {}
+    for ln in open(path):
+        if ":" in ln and not ln.startswith(("#", " ")):
+            k, v = ln.split(":", 1)
+            rec[k.strip()] = v.strip()
     if rec.get("source_sha256") != _sha(kernel_src):
         return None
-    return rec.get("hbm_bytes_per_launch")
+    return float(rec["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in rec else None
+
+
+def _r(v: float, nd: int):
+    """round(), with NaN (a leg that did not run) reported as null."""
+    return None if v != v else round(v, nd)
+
+
+def copy_calibration(nbytes: int = 1 << 30, reps: int = 3) -> int:
+    """A plain device-to-device copy of known size, the yardstick that scales the HBM byte
+    counters (FETCH_SIZE, WRITE_SIZE) of the layer's kernels."""
+    import torch
+
+    src = torch.full((nbytes,), 7, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes": nbytes, "reps": reps}), flush=True)
+    return 0
 
 
 def main() -> int:
@@ -56,13 +82,23 @@ def main() -> int:
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default=None)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-tokens", type=int, default=1024)
-    ap.add_argument("--cpu-weights", type=int, default=4096)
+    ap.add_argument("--no-extras", action="store_true",
+                    help="time only the hot path (skip the orbq_linear cross-check, the cold-cache "
+                         "rpbh_quantize run and the torch context); for profiler runs")
+    ap.add_argument("--settle", type=float, default=SETTLE_S,
+                    help="seconds of untimed steps before the warmup steps (clock settle)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="run only a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample tokens (default: all)")
+    ap.add_argument("--cpu-weights", type=int, default=None, help="oracle sample weight rows (default: all)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is data-parallel "
               "over tokens and the multi-GPU sharding is not built.", file=sys.stderr)
         return 2
+
+    if args.copy_calibration:
+        return copy_calibration()
 
     import numpy as np
     import torch
@@ -99,6 +135,15 @@ def main() -> int:
     def gemm():
         orbq.lut_gemm(x_codes, x_norms, cb_a, w_codes, w_norms, cb_w, L.d, out=Y)
 
+    # The GPU leaves its idle power state over the first tens of milliseconds of work: run the
+    # step for at least --settle seconds of wall time before the W warmup steps so that the timed steps
+    # see the steady-state clocks a serving loop runs at.
+    t_settle = time.perf_counter()
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(20):
+            quantize()
+            gemm()
+        torch.cuda.synchronize()
     for _ in range(args.warmup):
         quantize()
         gemm()
@@ -124,55 +169,57 @@ def main() -> int:
     q_bytes = L.n * (2 * L.d + L.d * L.bits_a // 8 + 4)
     value = flops / (ms_step * 1e-3) / 1e12
 
-    # ---- the same layer through the single orbq_linear entry point (cross-check)
-    for _ in range(3):
-        orbq.linear(X, rot, cb_a, w_codes, w_norms, cb_w, workspace=ws, out=Y)
-    torch.cuda.synchronize()
-    t2 = time.perf_counter()
-    for _ in range(args.steps):
-        orbq.linear(X, rot, cb_a, w_codes, w_norms, cb_w, workspace=ws, out=Y)
-    torch.cuda.synchronize()
-    linear_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+    linear_ms = q_cold_ms = ref_gemm_tflops = copy_gbps = float("nan")
+    if not args.no_extras:
+        # ---- the same layer through the single orbq_linear entry point (cross-check)
+        for _ in range(3):
+            orbq.linear(X, rot, cb_a, w_codes, w_norms, cb_w, workspace=ws, out=Y)
+        torch.cuda.synchronize()
+        t2 = time.perf_counter()
+        for _ in range(args.steps):
+            orbq.linear(X, rot, cb_a, w_codes, w_norms, cb_w, workspace=ws, out=Y)
+        torch.cuda.synchronize()
+        linear_ms = (time.perf_counter() - t2) * 1e3 / args.steps
 
-    # ---- rpbh_quantize with inputs rotated over > 2x the 256 MB Infinity Cache
-    nbuf = max(2, -(-2 * MALL_BYTES // (L.n * L.d * 2)))
-    bufs = [X] + [X.roll(k + 1, dims=0).contiguous() for k in range(nbuf - 1)]
-    reps = max(2, args.steps // nbuf) * nbuf
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    for b in bufs:
-        quantize(b)
-    torch.cuda.synchronize()
-    e0.record()
-    for k in range(reps):
-        quantize(bufs[k % nbuf])
-    e1.record()
-    torch.cuda.synchronize()
-    q_cold_ms = e0.elapsed_time(e1) / reps
-    del bufs
+        # ---- rpbh_quantize with inputs rotated over > 2x the 256 MB Infinity Cache
+        nbuf = max(2, -(-2 * MALL_BYTES // (L.n * L.d * 2)))
+        bufs = [X] + [X.roll(k + 1, dims=0).contiguous() for k in range(nbuf - 1)]
+        reps = max(2, args.steps // nbuf) * nbuf
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for b in bufs:
+            quantize(b)
+        torch.cuda.synchronize()
+        e0.record()
+        for k in range(reps):
+            quantize(bufs[k % nbuf])
+        e1.record()
+        torch.cuda.synchronize()
+        q_cold_ms = e0.elapsed_time(e1) / reps
+        del bufs
 
-    # ---- context: torch's bf16 GEMM of the same shape and a same-size copy
-    A = torch.randn((L.n, L.d), dtype=torch.bfloat16, device=dev)
-    B = torch.randn((L.d, L.m), dtype=torch.bfloat16, device=dev)
-    for _ in range(3):
-        torch.matmul(A, B, out=Y)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(20):
-        torch.matmul(A, B, out=Y)
-    e1.record()
-    torch.cuda.synchronize()
-    ref_gemm_tflops = flops / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12
-    src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
-    dst = torch.empty_like(src)
-    dst.copy_(src)
-    torch.cuda.synchronize()
-    e0.record()
-    for _ in range(10):
+        # ---- context: torch's bf16 GEMM of the same shape and a same-size copy
+        A = torch.randn((L.n, L.d), dtype=torch.bfloat16, device=dev)
+        B = torch.randn((L.d, L.m), dtype=torch.bfloat16, device=dev)
+        for _ in range(3):
+            torch.matmul(A, B, out=Y)
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(20):
+            torch.matmul(A, B, out=Y)
+        e1.record()
+        torch.cuda.synchronize()
+        ref_gemm_tflops = flops / (e0.elapsed_time(e1) / 20 * 1e-3) / 1e12
+        src = torch.empty((1 << 30,), dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
         dst.copy_(src)
-    e1.record()
-    torch.cuda.synchronize()
-    copy_gbps = 2 * src.numel() / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
-    del src, dst, A, B
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(10):
+            dst.copy_(src)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_gbps = 2 * src.numel() / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
+        del src, dst, A, B
 
     gemm_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "lut_gemm.hip")
     quant_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "rpbh_quantize.hip")
@@ -194,17 +241,17 @@ def main() -> int:
         "config": {"workload": name, "tokens": L.n, "d": L.d, "m": L.m, "bits_w": L.bits_w,
                    "bits_a": L.bits_a, "block": L.block, "y_dtype": "bf16"},
         "rpbh_quantize_GBps": round(q_gbps, 1),
-        "rpbh_quantize_cold_GBps": round(q_bytes / (q_cold_ms * 1e-3) / 1e9, 1),
+        "rpbh_quantize_cold_GBps": _r(q_bytes / (q_cold_ms * 1e-3) / 1e9, 1),
         "kernel_ms": {"rpbh_quantize": round(q_ms, 5), "lut_gemm": round(g_ms, 5),
-                      "rpbh_quantize_cold": round(q_cold_ms, 5), "orbq_linear_call": round(linear_ms, 5)},
+                      "rpbh_quantize_cold": _r(q_cold_ms, 5), "orbq_linear_call": _r(linear_ms, 5)},
         "roofline": {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(g_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": _traffic(gemm_src, "lut_gemm", name)},
         "rpbh_roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": round(q_gbps / HBM_PEAK_GBPS, 4),
                           "traffic": _traffic(quant_src, "rpbh_quantize", name)},
-        "context": {"torch_bf16_matmul_TFLOPs": round(ref_gemm_tflops, 1),
-                    "torch_copy_GBps": round(copy_gbps, 1)},
+        "context": {"torch_bf16_matmul_TFLOPs": _r(ref_gemm_tflops, 1),
+                    "torch_copy_GBps": _r(copy_gbps, 1)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L, X_bits, W_bits, perm, signs, args.cpu_tokens, args.cpu_weights)
@@ -213,28 +260,34 @@ def main() -> int:
 
 
 def cpu_baseline(L, X_bits, W_bits, perm, signs, n_tok, n_w):
-    """The oracle as it stands (numpy float64) on a bounded sample of the same layer: the
-    first n_tok tokens against the first n_w weight rows (weights folded untimed)."""
+    """The oracle as it stands (numpy float64) on a bounded sample of the same layer: the first
+    n_tok tokens against the first n_w weight rows (default: the whole layer; weights folded
+    untimed), repeated until CPU_SECONDS have passed; throughput over all repetitions."""
     import numpy as np
     from threadpoolctl import threadpool_info
 
     import oracle
     import workloads
 
-    n_tok, n_w = min(n_tok, L.n), min(n_w, L.m)
+    n_tok = L.n if n_tok is None else min(n_tok, L.n)
+    n_w = L.m if n_w is None else min(n_w, L.m)
     Pi = oracle.rpbh_matrix(L.d, L.block, perm, signs)
     c_a = oracle.lloyd_max(L.d, L.bits_a).astype(np.float32)
     c_w = oracle.lloyd_max(L.d, L.bits_w).astype(np.float32)
     kw, r, _, _ = oracle.fold_weights(workloads.f64_from_bf16_bits(W_bits[:n_w]), Pi, c_w)
     Xs = workloads.f64_from_bf16_bits(X_bits[:n_tok])
+    reps = 0
     t0 = time.perf_counter()
-    oracle.orbq_linear(Xs, Pi, c_a, kw, r, c_w)
+    while reps == 0 or time.perf_counter() - t0 < CPU_SECONDS:
+        oracle.orbq_linear(Xs, Pi, c_a, kw, r, c_w)
+        reps += 1
     dt = time.perf_counter() - t0
     threads = max([p.get("num_threads", 1) for p in threadpool_info()] + [1])
-    return {"value": round(2.0 * n_tok * n_w * L.d / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle", "seconds": round(dt, 2),
-            "sample": f"first {n_tok} tokens x first {n_w} weight rows of {L.name} (d={L.d}); "
-                      "rotate + quantize + float64 dequantised product"}
+    return {"value": round(2.0 * n_tok * n_w * L.d * reps / dt / 1e12, 5), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle", "seconds": round(dt, 2), "repetitions": reps,
+            "sample": f"{n_tok} tokens x {n_w} weight rows of {L.name} (d={L.d}), the online layer "
+                      "(rotate + quantize + float64 dequantised product) repeated for at least "
+                      f"{CPU_SECONDS:.0f} s"}
 
 
 if __name__ == "__main__":

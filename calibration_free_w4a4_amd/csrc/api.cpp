@@ -58,6 +58,8 @@ int check_rot(const orbq_rpbh* rot, int64_t d, const char* what) {
   if (rot->block != 64 && rot->block != 128)
     return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not in {64,128}", what, rot->block);
   if (d % rot->block) return fail(ORBQ_ERR_INVALID_ARG, "%s: d=%lld not a multiple of block %d", what, (long long)d, rot->block);
+  if (!aligned(rot->perm, 16) || !aligned(rot->signs, 16))
+    return fail(ORBQ_ERR_ALIGNMENT, "%s: rotation arrays must be 16-byte aligned", what);
   return ORBQ_OK;
 }
 

@@ -1,6 +1,11 @@
 /*
  * orbq.h -- C ABI of the OrbitQuant quantized linear layer on AMD Instinct MI355X (gfx950).
  *
+ * Pages cited: "OrbitQuant: Data-Agnostic Quantization for Image and Video Diffusion
+ * Transformers" (summary page on picx.dev; cited as "OrbitQuant summary" with its section
+ * titles) and the TurboQuant slide deck ("TurboQuant: Online Vector Quantization with
+ * Near-optimal Distortion Rate", docswell; cited by slide number "Page. N").
+ *
  * What the library computes (OrbitQuant summary, picx.dev, "Methodology"):
  *   offline  "Offline Weight Quantization": W' = W Pi^T, r'_i = ||w'_i||, codes of
  *            w'_i / r'_i under a Lloyd-Max codebook, r' stored in bf16.
@@ -72,7 +77,9 @@ typedef enum { ORBQ_F32 = 0, ORBQ_BF16 = 1 } orbq_dtype;
  *   d      dimension, multiple of block
  *   block  Hadamard block size h (64 or 128)
  *   perm   [device] int32[d], a permutation of 0..d-1: (P x)[j] = x[perm[j]]
- *   signs  [device] int8[d], each +1 or -1, applied to position j after the permutation */
+ *   signs  [device] int8[d], each +1 or -1, applied to position j after the permutation
+ * Both arrays 16-byte aligned (ORBQ_ERR_ALIGNMENT otherwise); they must stay valid until the
+ * calls that use them have completed on their stream. */
 typedef struct {
   int32_t d;
   int32_t block;

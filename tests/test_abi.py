@@ -121,6 +121,8 @@ def test_argument_errors_return_before_launch(cb):
     assert q(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), float("nan"), P, P, None) == -1  # eps
     rot32 = orbq._Rpbh(d, 32, 0x1000, 0x2000)
     assert q(P, 8, d, d, ctypes.byref(rot32), ctypes.byref(c4), 1e-8, P, P, None) == -2        # block
+    rot_mis = orbq._Rpbh(d, 64, 0x1004, 0x2000)
+    assert q(P, 8, d, d, ctypes.byref(rot_mis), ctypes.byref(c4), 1e-8, P, P, None) == -3      # perm alignment
     c4d, keep = _cb_struct(cb(d, 4), 512, 4)
     assert q(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4d), 1e-8, P, P, None) == -1         # codebook d
     c3, keep3 = _cb_struct(np.linspace(-1, 1, 8), d, 3)
