@@ -5,18 +5,27 @@
 // rotation cancels.  The product is a dense contraction over d, so it runs on the matrix cores.
 //
 // Kernel layout (gfx950, wave64, 512 threads = 8 waves, two per SIMD):
-//   * workgroup tile 256 tokens x 256 weight rows, K tile of 32; each wave computes 64 x 128
-//     with v_mfma_f32_32x32x16_bf16 and fp32 accumulators (2 x 4 tiles of 32 x 32).
-//   * waves 0-3 load the 256 token code rows of the K tile, waves 4-7 the 256 weight code rows
-//     (8..24 bytes per thread), decode them to bf16 centroid values and store them to LDS; the
-//     MFMA operands are 16-byte LDS reads.  Code rows are prefetched two K tiles ahead in
-//     registers; LDS is double buffered, one barrier per K tile.
+//   * workgroup tile BM tokens x BN weight rows (384 x 192 or 256 x 256, chosen on the host so
+//     that the tiles fill the compute units in whole rounds), K tile of 64; the waves form a
+//     4 x 2 grid, each computing (BM/4) x (BN/2) with v_mfma_f32_32x32x16_bf16 and fp32
+//     accumulators.
+//   * staging: a K tile holds (BM + BN) code rows of 64 codes, i.e. (BM + BN) * 8 units of 8
+//     codes.  Thread t owns unit column t % 8 of rows t / 8 + 64 i, i < (BM + BN) / 64, so every
+//     thread decodes the same number of units.  Code rows are read with buffer loads (rows past
+//     the end read as zero and are never stored), two K tiles ahead in registers.
 //   * decode of 4-bit codes: v_perm_b32 byte lookups into the 8 bf16 magnitudes (held in four
 //     registers) plus the sign bit; 2-bit codes use a 256-entry LDS table per code byte, 6-bit
 //     codes a 4096-entry LDS table per code pair.  Every decoder writes the 8 values of a
 //     16-byte chunk in the order k = 0,2,4,6,1,3,5,7, so A and B agree on k.
+//   * LDS: two stages of [BM + BN][64] bf16, 128-byte rows whose 16-byte chunks are xor-swizzled
+//     by (row >> 1) & 7; the MFMA fragment reads (32 rows at one chunk) and the staging stores
+//     (8 rows x 8 chunks per wave) are free of bank conflicts.  One barrier per K tile.
+//   * schedule: inside a K tile every second MFMA is followed by half of one unit's decode (and
+//     its LDS store), so the decode of the next K tile runs in the shadow of the matrix cores.
 //   * epilogue: Y = acc * s_i * r'_j in fp32, stored as fp32 or bf16 (round to nearest even).
 #include <hip/hip_runtime.h>
+
+#include <algorithm>
 
 #include "internal.h"
 
@@ -25,9 +34,25 @@ namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int v2u_t __attribute__((ext_vector_type(2)));
 
-constexpr int BM = 256, BN = 256, KT = 32;
+constexpr int KT = 64;          // K tile (codes)
+constexpr int kRow = KT * 2;    // bytes of one staged bf16 row
 constexpr int kThreads = 512;
+constexpr uint32_t kBufWord3 = 0x00020000u;  // raw (untyped) buffer resource, gfx9 family
+
+template <int BM_, int BN_>
+struct Cfg {
+  static constexpr int BM = BM_, BN = BN_;
+  static constexpr int TM = BM / 4, TN = BN / 2;    // per-wave tile (4 x 2 waves)
+  static constexpr int TI = TM / 32, TJ = TN / 32;  // 32 x 32 MFMA blocks per wave
+  static constexpr int U = (BM + BN) / 64;          // 8-code units per thread per K tile
+  static constexpr int UA = BM / 64;                // of which in the token tile
+  static constexpr int NM = TI * TJ;                // MFMAs per wave per 16-deep k step
+  static constexpr int SA = BM * kRow, SB = BN * kRow;  // bytes of one stage of A / B
+  static constexpr int LDS = 2 * (SA + SB);
+  static_assert(2 * U == 4 * NM / 2, "one half-unit of decode per two MFMAs");
+};
 
 struct GemmArgs {
   const uint8_t* xc;
@@ -35,8 +60,9 @@ struct GemmArgs {
   const uint8_t* wc;
   const uint16_t* wn;
   void* Y;
-  int64_t n, m, d, ldy;
-  int64_t xrow_bytes, wrow_bytes;
+  int64_t n, m, ldy;
+  int32_t xrow_bytes, wrow_bytes;
+  int32_t nk;  // K tiles
   int32_t tiles_n, tiles_m;
   // 4-bit decode tables: low / high bytes of the 8 bf16 magnitudes, 4 per register
   uint32_t lt_lo_a, lt_hi_a, ht_lo_a, ht_hi_a;
@@ -49,20 +75,30 @@ struct Tab4 {
   uint32_t lt_lo, lt_hi, ht_lo, ht_hi;
 };
 
-__device__ __forceinline__ uint4 decode4(uint32_t X, const Tab4& t) {
+// 4-bit, in two halves: (1) magnitude bytes of the even and odd codes, (2) signs and bf16 pairs
+struct Half4 {
+  uint32_t le, he, lo, ho;
+};
+
+__device__ __forceinline__ Half4 decode4_a(uint32_t X, const Tab4& t) {
   const uint32_t se = X & 0x07070707u;
   const uint32_t so = (X >> 4) & 0x07070707u;
-  const uint32_t le = __builtin_amdgcn_perm(t.lt_hi, t.lt_lo, se);
-  uint32_t he = __builtin_amdgcn_perm(t.ht_hi, t.ht_lo, se);
-  const uint32_t lo = __builtin_amdgcn_perm(t.lt_hi, t.lt_lo, so);
-  uint32_t ho = __builtin_amdgcn_perm(t.ht_hi, t.ht_lo, so);
-  he |= (X << 4) & 0x80808080u;  // sign = bit 3 of each code
-  ho |= X & 0x80808080u;
+  Half4 h;
+  h.le = __builtin_amdgcn_perm(t.lt_hi, t.lt_lo, se);
+  h.he = __builtin_amdgcn_perm(t.ht_hi, t.ht_lo, se);
+  h.lo = __builtin_amdgcn_perm(t.lt_hi, t.lt_lo, so);
+  h.ho = __builtin_amdgcn_perm(t.ht_hi, t.ht_lo, so);
+  return h;
+}
+
+__device__ __forceinline__ uint4 decode4_b(uint32_t X, Half4 h) {
+  const uint32_t he = h.he | ((X << 4) & 0x80808080u);  // sign = bit 3 of each code
+  const uint32_t ho = h.ho | (X & 0x80808080u);
   uint4 r;
-  r.x = __builtin_amdgcn_perm(he, le, 0x05010400u);  // (e0, e2)
-  r.y = __builtin_amdgcn_perm(he, le, 0x07030602u);  // (e4, e6)
-  r.z = __builtin_amdgcn_perm(ho, lo, 0x05010400u);  // (e1, e3)
-  r.w = __builtin_amdgcn_perm(ho, lo, 0x07030602u);  // (e5, e7)
+  r.x = __builtin_amdgcn_perm(he, h.le, 0x05010400u);  // (e0, e2)
+  r.y = __builtin_amdgcn_perm(he, h.le, 0x07030602u);  // (e4, e6)
+  r.z = __builtin_amdgcn_perm(ho, h.lo, 0x05010400u);  // (e1, e3)
+  r.w = __builtin_amdgcn_perm(ho, h.lo, 0x07030602u);  // (e5, e7)
   return r;
 }
 
@@ -92,69 +128,7 @@ __device__ __forceinline__ uint16_t mag_signed(const uint16_t* mag, uint32_t cod
   return static_cast<uint16_t>(mag[code & (half - 1)] | ((code & half) ? 0x8000u : 0u));
 }
 
-// Loads the K-tile bytes of one code row and decodes them into 4 chunks of 8 bf16.
-template <int B>
-struct RowTile;
-
-template <>
-struct RowTile<4> {
-  uint4 raw;
-  __device__ __forceinline__ void load(const uint8_t* row, int kt) {
-    raw = *reinterpret_cast<const uint4*>(row + kt * 16);
-  }
-  __device__ __forceinline__ void decode(uint4 out[4], const Tab4& t, const void*) const {
-    out[0] = decode4(raw.x, t);
-    out[1] = decode4(raw.y, t);
-    out[2] = decode4(raw.z, t);
-    out[3] = decode4(raw.w, t);
-  }
-};
-
-template <>
-struct RowTile<2> {
-  uint2 raw;
-  __device__ __forceinline__ void load(const uint8_t* row, int kt) {
-    raw = *reinterpret_cast<const uint2*>(row + kt * 8);
-  }
-  __device__ __forceinline__ void decode(uint4 out[4], const Tab4&, const void* lut) const {
-    const uint2* l = static_cast<const uint2*>(lut);
-    out[0] = decode2(raw.x & 0xFFFF, l);
-    out[1] = decode2(raw.x >> 16, l);
-    out[2] = decode2(raw.y & 0xFFFF, l);
-    out[3] = decode2(raw.y >> 16, l);
-  }
-};
-
-template <>
-struct RowTile<6> {
-  uint2 r0, r1, r2;  // 24 bytes
-  __device__ __forceinline__ void load(const uint8_t* row, int kt) {
-    const uint2* p = reinterpret_cast<const uint2*>(row + kt * 24);
-    r0 = p[0];
-    r1 = p[1];
-    r2 = p[2];
-  }
-  __device__ __forceinline__ void decode(uint4 out[4], const Tab4&, const void* lut) const {
-    const uint32_t* l = static_cast<const uint32_t*>(lut);
-    // 8 codes per 6 bytes: words w0..w5
-    out[0] = decode6(r0.x, r0.y & 0xFFFF, l);
-    out[1] = decode6((r0.y >> 16) | (r1.x << 16), r1.x >> 16, l);
-    out[2] = decode6(r1.y, r2.x & 0xFFFF, l);
-    out[3] = decode6((r2.x >> 16) | (r2.y << 16), r2.y >> 16, l);
-  }
-};
-
-// Row swizzle of the 16-byte chunks of a [256][32] bf16 tile (64-byte rows): chunk c of row r
-// sits at c ^ swz(r).  swz takes distinct values on rows {r, r+2, r+4, r+6} and on rows
-// {r, r+4, r+8, r+12}, so 16-byte accesses of any 8 (or 16) consecutive rows at one chunk hit
-// distinct banks whether the LDS serves 128 or 256 bytes per clock.
-__device__ __forceinline__ uint32_t swz(uint32_t r) { return ((r >> 1) + (r >> 3)) & 3; }
-
-__device__ __forceinline__ uint32_t tile_off(int row, int chunk) {
-  return static_cast<uint32_t>(row * 64 + ((chunk ^ swz(row)) << 4));
-}
-
-constexpr size_t lut_bytes_dev(int bits) { return bits == 2 ? 256 * 8 : bits == 6 ? 4096 * 4 : 0; }
+constexpr int lut_bytes_dev(int bits) { return bits == 2 ? 256 * 8 : bits == 6 ? 4096 * 4 : 0; }
 
 template <int BITS>
 __device__ __forceinline__ void build_lut(const uint16_t* mag, unsigned char* p, int tid) {
@@ -172,14 +146,66 @@ __device__ __forceinline__ void build_lut(const uint16_t* mag, unsigned char* p,
   }
 }
 
-template <int BA, int BW, bool OUT_BF16>
-__global__ __launch_bounds__(kThreads, 1) void k_lut_gemm(GemmArgs a) {
+// One operand's code unit (8 codes) of a K tile: raw bits in registers, decoded in two halves.
+// `off` is the unit's byte offset from the resource base (row * row_bytes + unit column bytes).
+template <int B>
+struct Unit;
+
+template <>
+struct Unit<4> {
+  static constexpr int kStep = KT / 2;  // bytes per K tile of a row
+  uint32_t w;
+  Half4 h;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    w = __builtin_amdgcn_raw_buffer_load_b32(rs, off, 0, 0);
+  }
+  __device__ __forceinline__ void first(const Tab4& t, const void*) { h = decode4_a(w, t); }
+  __device__ __forceinline__ uint4 second(const Tab4&, const void*) const { return decode4_b(w, h); }
+  static __device__ __forceinline__ uint32_t col_bytes(uint32_t c) { return 4 * c; }
+};
+
+template <>
+struct Unit<2> {
+  static constexpr int kStep = KT / 4;
+  uint32_t w;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    w = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+  }
+  __device__ __forceinline__ void first(const Tab4&, const void*) {}
+  __device__ __forceinline__ uint4 second(const Tab4&, const void* lut) const {
+    return decode2(w, static_cast<const uint2*>(lut));
+  }
+  static __device__ __forceinline__ uint32_t col_bytes(uint32_t c) { return 2 * c; }
+};
+
+template <>
+struct Unit<6> {
+  static constexpr int kStep = KT * 6 / 8;
+  v2u_t w;        // 8 bytes read from a 4-byte aligned offset; the unit starts 0 or 2 bytes in
+  uint32_t sh;    // 0 or 16: bit offset of the unit in w
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
+    w = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
+  }
+  __device__ __forceinline__ void first(const Tab4&, const void*) {}
+  __device__ __forceinline__ uint4 second(const Tab4&, const void* lut) const {
+    const uint32_t lo = __builtin_amdgcn_alignbit(w.y, w.x, sh);
+    const uint32_t hi = (w.y >> sh) & 0xFFFFu;
+    return decode6(lo, hi, static_cast<const uint32_t*>(lut));
+  }
+  static __device__ __forceinline__ uint32_t col_bytes(uint32_t c) { return (6 * c) & ~3u; }
+};
+
+// chunk swizzle of a staged row: chunk c of row r sits at c ^ ((r >> 1) & 7)
+__device__ __forceinline__ uint32_t swz(uint32_t r) { return (r >> 1) & 7; }
+
+template <int BA, int BW, bool OUT_BF16, int BM, int BN>
+__global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
+  using C = Cfg<BM, BN>;
   extern __shared__ __align__(16) unsigned char smem[];
-  unsigned char* As = smem;                    // [2][256][32] bf16
-  unsigned char* Bs = smem + 2 * BM * KT * 2;  // [2][256][32] bf16
-  unsigned char* lut = Bs + 2 * BN * KT * 2;
+  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1][2-/6-bit tables]
+  unsigned char* lut = smem + C::LDS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave & 3, wn = wave >> 2;     // 64-row band of tokens, 128-row band of weights
+  const int wm = wave & 3, wn = wave >> 2;
 
   // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give each XCD a
   // contiguous band of tiles (neighbouring tiles share code rows in that XCD's L2)
@@ -190,11 +216,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_lut_gemm(GemmArgs a) {
   const int64_t row0 = static_cast<int64_t>(tn) * BM;  // token rows
   const int64_t col0 = static_cast<int64_t>(tm) * BN;  // weight rows
 
-  // decode tables: 2- and 6-bit codes decode through LDS tables built from the magnitudes
-  uint16_t* mags = reinterpret_cast<uint16_t*>(lut);  // [0, 32): activations, [32, 64): weights
-  unsigned char* lut_a = lut + 128;
-  unsigned char* lut_w = lut_a + lut_bytes_dev(BA);
+  // decode tables for 2- and 6-bit codes, built from the magnitudes (staged through the first
+  // bytes of the B region, which the first K tile overwrites only after the next barrier)
+  unsigned char* lut_a = lut;
+  unsigned char* lut_w = lut + lut_bytes_dev(BA);
   if constexpr (BA != 4 || BW != 4) {
+    uint16_t* mags = reinterpret_cast<uint16_t*>(smem + 2 * C::SA);
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
       if (tid == r) mags[r] = a.mag_a[r];
@@ -203,124 +230,220 @@ __global__ __launch_bounds__(kThreads, 1) void k_lut_gemm(GemmArgs a) {
     __syncthreads();
     build_lut<BA>(mags, lut_a, tid);
     build_lut<BW>(mags + 32, lut_w, tid);
+    __syncthreads();
   }
-
-  // loader role: threads 0-255 stage token row tid, threads 256-511 weight row tid-256
-  const bool loads_a = tid < BM;
-  const int lrow = loads_a ? tid : tid - BM;
-  const uint8_t* arow = a.xc + min(row0 + lrow, a.n - 1) * a.xrow_bytes;  // rows past the end are
-  const uint8_t* brow = a.wc + min(col0 + lrow, a.m - 1) * a.wrow_bytes;  // computed and discarded
   const Tab4 ta{a.lt_lo_a, a.lt_hi_a, a.ht_lo_a, a.ht_hi_a};
   const Tab4 tw{a.lt_lo_w, a.lt_hi_w, a.ht_lo_w, a.ht_hi_w};
-  const int nk = static_cast<int>(a.d / KT);
 
-  f32x16_t acc[2][4];
+  // ---- staging role: unit column c of rows rr + 64 i of the (A rows, then B rows) tile
+  const uint32_t c = tid & 7, rr = tid >> 3;
+  const uint32_t xrow = static_cast<uint32_t>(a.xrow_bytes), wrow = static_cast<uint32_t>(a.wrow_bytes);
+  const uint32_t xoff0 = rr * xrow + Unit<BA>::col_bytes(c), woff0 = rr * wrow + Unit<BW>::col_bytes(c);
+  const uint32_t wofs = rr * kRow + ((c ^ swz(rr)) << 4);  // swz(rr + 64 i) = swz(rr)
+  // the odd / even parity of the (virtual) first tile: an odd tile count is padded with a
+  // leading all-zero tile so that the loop runs in pairs
+  const int odd = a.nk & 1;
+  const int nv = a.nk + odd;
+  const uint8_t* xbase = a.xc + row0 * xrow;
+  const uint8_t* wbase = a.wc + col0 * wrow;
+  const int64_t xrem = (a.n - row0) * static_cast<int64_t>(xrow);
+  const int64_t wrem = (a.m - col0) * static_cast<int64_t>(wrow);
+  auto rsrc = [](const uint8_t* base, int64_t rem, int kt, int step) {
+    const int64_t left = rem - static_cast<int64_t>(kt) * step;
+    const uint32_t nrec = left > 0xFFFFFFF0ll ? 0xFFFFFFF0u : static_cast<uint32_t>(left);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(base + static_cast<int64_t>(kt) * step), 0,
+                                             nrec, kBufWord3);
+  };
+  // real K tile of virtual tile v (clamped into range: loads past the last tile are discarded)
+  auto real_tile = [&](int v) { return min(max(v - odd, 0), a.nk - 1); };
+
+  struct Set {
+    Unit<BA> ua[C::UA];
+    Unit<BW> ub[C::U - C::UA];
+  };
+  Set s0, s1;
+  auto load_set = [&](Set& s, int v) {
+    const int kt = real_tile(v);
+    const auto rx = rsrc(xbase, xrem, kt, Unit<BA>::kStep);
+    const auto rw = rsrc(wbase, wrem, kt, Unit<BW>::kStep);
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < C::UA; ++i) s.ua[i].load(rx, xoff0 + 64u * i * xrow);
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int i = 0; i < C::U - C::UA; ++i) s.ub[i].load(rw, woff0 + 64u * i * wrow);
+  };
+  if constexpr (BA == 6) {
+#pragma unroll
+    for (int i = 0; i < C::UA; ++i) { s0.ua[i].sh = (c & 1) * 16; s1.ua[i].sh = (c & 1) * 16; }
+  }
+  if constexpr (BW == 6) {
+#pragma unroll
+    for (int i = 0; i < C::U - C::UA; ++i) { s0.ub[i].sh = (c & 1) * 16; s1.ub[i].sh = (c & 1) * 16; }
+  }
+
+  // half-step h (0 <= h < 2U) of the decode of set s into stage buf: unit h / 2, half h % 2
+  auto half_step = [&](Set& s, int buf, int h) {
+    const int u = h >> 1;
+    if (u < C::UA) {
+      if ((h & 1) == 0) s.ua[u].first(ta, lut_a);
+      else {
+        const uint4 v = s.ua[u].second(ta, lut_a);
+        *reinterpret_cast<uint4*>(smem + buf * C::SA + wofs + u * (64 * kRow)) = v;
+      }
+    } else {
+      const int ub = u - C::UA;
+      if ((h & 1) == 0) s.ub[ub].first(tw, lut_w);
+      else {
+        const uint4 v = s.ub[ub].second(tw, lut_w);
+        *reinterpret_cast<uint4*>(smem + 2 * C::SA + buf * C::SB + wofs + ub * (64 * kRow)) = v;
+      }
+    }
+  };
+
+  f32x16_t acc[C::TI][C::TJ];
+#pragma unroll
+  for (int i = 0; i < C::TI; ++i)
+#pragma unroll
+    for (int j = 0; j < C::TJ; ++j)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+  // fragment addresses: row (band + 32 i + l32), chunk (2 ks + g) xor the row swizzle; the
+  // swizzle depends only on l32 (bands are multiples of 32 rows), so i, j and the stage are
+  // immediate offsets
   const int g = lane >> 5, l32 = lane & 31;
-  // Fragment addresses: row (band + 32 i + l32), chunk (2 ks + g) xor the row swizzle.  The
-  // swizzle depends only on l32, so per lane two bases (ks = 0, 1) per operand suffice and
-  // the tile index i / j and the buffer become immediate offsets.
-  const uint32_t sw = swz(l32);  // the band offsets are multiples of 32 rows: swz(band + l32) = swz(l32)
-  const uint32_t a_base = (wm * 64 + l32) * 64, b_base = (wn * 128 + l32) * 64;
-  const uint32_t ch0 = ((0u | g) ^ sw) << 4, ch1 = ((2u | g) ^ sw) << 4;
-  const uint32_t a_off[2] = {a_base + ch0, a_base + ch1};
-  const uint32_t b_off[2] = {b_base + ch0 + 2 * BM * KT * 2, b_base + ch1 + 2 * BM * KT * 2};
-  auto compute = [&](int buf) {
+  const uint32_t sw = swz(l32);
+  uint32_t a_off[4], b_off[4];
 #pragma unroll
-    for (int ks = 0; ks < 2; ++ks) {
-      bf16x8_t fa[2], fb[4];
+  for (int ks = 0; ks < 4; ++ks) {
+    const uint32_t ch = ((2u * ks + g) ^ sw) << 4;
+    a_off[ks] = (wm * C::TM + l32) * kRow + ch;
+    b_off[ks] = 2 * C::SA + (wn * C::TN + l32) * kRow + ch;
+  }
+  struct Frags {
+    bf16x8_t fa[C::TI], fb[C::TJ];
+  };
+  auto read_frags = [&](Frags& f, int buf, int ks) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        fa[i] = *reinterpret_cast<const bf16x8_t*>(smem + a_off[ks] + buf * (BM * KT * 2) + i * (32 * 64));
+    for (int i = 0; i < C::TI; ++i)
+      f.fa[i] = *reinterpret_cast<const bf16x8_t*>(smem + a_off[ks] + buf * C::SA + i * (32 * kRow));
 #pragma unroll
-      for (int j = 0; j < 4; ++j)
-        fb[j] = *reinterpret_cast<const bf16x8_t*>(smem + b_off[ks] + buf * (BN * KT * 2) + j * (32 * 64));
+    for (int j = 0; j < C::TJ; ++j)
+      f.fb[j] = *reinterpret_cast<const bf16x8_t*>(smem + b_off[ks] + buf * C::SB + j * (32 * kRow));
+  };
+
+  // one K tile: MFMAs on stage `buf`, with the decode of set `s` into stage 1 - buf in their
+  // shadow (half a unit after every second MFMA)
+  auto ktile = [&](int buf, Set& s) {
+    Frags f[2];
+    read_frags(f[0], buf, 0);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+    for (int ks = 0; ks < 4; ++ks) {
+      if (ks < 3) read_frags(f[(ks + 1) & 1], buf, ks + 1);
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(fa[i], fb[j], acc[i][j], 0, 0, 0);
+      for (int p = 0; p < C::NM; ++p) {
+        const int i = p / C::TJ, j = p % C::TJ;
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].fa[i], f[ks & 1].fb[j], acc[i][j], 0, 0, 0);
+        const int q = ks * C::NM + p;
+        if (q & 1) half_step(s, 1 - buf, q >> 1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
     }
   };
 
-  // Main loop, specialised per loader role (waves 0-3 stage token rows, waves 4-7 weight rows;
-  // both paths hit the same barriers).  Two K tiles are in flight in registers; the loop is
-  // unrolled by two so that each register set keeps fixed registers.
-  auto main_loop = [&](auto& r0, auto& r1, const uint8_t* crow, const Tab4& tab, const void* lutp,
-                       unsigned char* tbase) {
-    auto stage = [&](int buf, const auto& rt) {
-      uint4 cv[4];
-      rt.decode(cv, tab, lutp);
-      unsigned char* t = tbase + buf * (BM * KT * 2);
+  // ---- prologue: codes of virtual tiles 0 and 1 in registers, tile 0 staged (all zero when it
+  // is the padding tile of an odd tile count)
+  load_set(s0, 0);
+  load_set(s1, 1);
+  if (odd) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) *reinterpret_cast<uint4*>(t + tile_off(lrow, c)) = cv[c];
-    };
-    r0.load(crow, 0);
-    r1.load(crow, 1);
-    __syncthreads();  // decode tables built
-    stage(0, r0);
-    __syncthreads();
-    // d is a multiple of 64, so nk = d / 32 is even and both halves always run.  The loads and
-    // stages are unconditional (tile indices clamped; the extra stage at the end writes a buffer
-    // nobody reads again) so that the compiler can count outstanding loads exactly and waits only
-    // for the tile it decodes, not for the one just issued.
-    for (int kt = 0; kt < nk; kt += 2) {
-      r0.load(crow, min(kt + 2, nk - 1));
-      compute(0);
-      stage(1, r1);
-      __syncthreads();
-      r1.load(crow, min(kt + 3, nk - 1));
-      compute(1);
-      stage(0, r0);
-      __syncthreads();
-    }
-  };
-  if (loads_a) {
-    RowTile<BA> r0, r1;
-    main_loop(r0, r1, arow, ta, lut_a, As);
+    for (int u = 0; u < C::UA; ++u)
+      *reinterpret_cast<uint4*>(smem + wofs + u * (64 * kRow)) = make_uint4(0, 0, 0, 0);
+#pragma unroll
+    for (int u = 0; u < C::U - C::UA; ++u)
+      *reinterpret_cast<uint4*>(smem + 2 * C::SA + wofs + u * (64 * kRow)) = make_uint4(0, 0, 0, 0);
   } else {
-    RowTile<BW> r0, r1;
-    main_loop(r0, r1, brow, tw, lut_w, Bs);
+#pragma unroll
+    for (int h = 0; h < 2 * C::U; ++h) half_step(s0, 0, h);
+  }
+  __syncthreads();
+
+  for (int v = 0; v < nv; v += 2) {
+    load_set(s0, v + 2);
+    ktile(0, s1);  // MFMAs on tile v, decode of tile v + 1
+    __syncthreads();
+    load_set(s1, v + 3);
+    ktile(1, s0);  // MFMAs on tile v + 1, decode of tile v + 2
+    __syncthreads();
   }
 
-  // epilogue: D[row][col] of a 32x32 tile: col = lane % 32, row = 8*(r/4) + 4*(lane/32) + r%4
+  // ---- epilogue: D[row][col] of a 32x32 tile: col = lane % 32, row = 8*(r/4) + 4*(lane/32) + r%4
   const bool full = row0 + BM <= a.n && col0 + BN <= a.m;
-  float rn[4];
-  int64_t cols[4];
+  constexpr int esz = OUT_BF16 ? 2 : 4;
+  float rn[C::TJ];
+  if (full) {
+    // whole tile in range: rows of a 32-row block are (r-dependent, uniform) scalar offsets,
+    // columns per-lane vector offsets, so the stores need no per-element address arithmetic;
+    // bf16 pairs of adjacent rows are rounded together (v_cvt_pk_bf16_f32, nearest even)
+    const int64_t ldy = a.ldy;
+    unsigned char* ybase = static_cast<unsigned char*>(a.Y) + (row0 * ldy + col0) * esz;
+    const __amdgpu_buffer_rsrc_t ys = __builtin_amdgcn_make_buffer_rsrc(ybase, 0, 0xFFFFFFF0u, kBufWord3);
+    uint32_t voff[C::TJ];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    cols[j] = col0 + wn * 128 + 32 * j + l32;
-    rn[j] = (full || cols[j] < a.m) ? __builtin_bit_cast(float, static_cast<uint32_t>(a.wn[cols[j]]) << 16) : 0.0f;
+    for (int j = 0; j < C::TJ; ++j) {
+      const int col = wn * C::TN + 32 * j + l32;
+      rn[j] = __builtin_bit_cast(float, static_cast<uint32_t>(a.wn[col0 + col]) << 16);
+      voff[j] = static_cast<uint32_t>(((wm * C::TM + 4 * g) * ldy + col) * esz);
+    }
+#pragma unroll
+    for (int i = 0; i < C::TI; ++i) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2) {
+        const int rr0 = 32 * i + 8 * (r >> 2) + (r & 3);  // row within the wave band (less 4 g)
+        const int64_t row = row0 + wm * C::TM + rr0 + 4 * g;
+        const float s0 = a.xs[row], s1 = a.xs[row + 1];
+        const int so0 = static_cast<int>(rr0 * ldy * esz), so1 = static_cast<int>((rr0 + 1) * ldy * esz);
+#pragma unroll
+        for (int j = 0; j < C::TJ; ++j) {
+          const float v0 = acc[i][j][r] * s0 * rn[j], v1 = acc[i][j][r + 1] * s1 * rn[j];
+          if constexpr (OUT_BF16) {
+            typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+            const bf16x2_t p = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
+            const uint32_t u = __builtin_bit_cast(uint32_t, p);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(u), ys, voff[j], so0, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(u >> 16), ys, voff[j], so1, 0);
+          } else {
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v0), ys, voff[j], so0, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v1), ys, voff[j], so1, 0);
+          }
+        }
+      }
+    }
+    return;
+  }
+  // edge tile: per-element bounds checks
+  int64_t cols[C::TJ];
+#pragma unroll
+  for (int j = 0; j < C::TJ; ++j) {
+    cols[j] = col0 + wn * C::TN + 32 * j + l32;
+    rn[j] = cols[j] < a.m ? __builtin_bit_cast(float, static_cast<uint32_t>(a.wn[cols[j]]) << 16) : 0.0f;
   }
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
+  for (int i = 0; i < C::TI; ++i) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int64_t row = row0 + wm * 64 + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
-      if (!full && row >= a.n) continue;
+      const int64_t row = row0 + wm * C::TM + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
+      if (row >= a.n) continue;
       const float sr = a.xs[row];
       if constexpr (OUT_BF16) {
-        uint16_t* yrow = reinterpret_cast<uint16_t*>(a.Y) + row * a.ldy;
+        __bf16* yrow = reinterpret_cast<__bf16*>(a.Y) + row * a.ldy;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (!full && cols[j] >= a.m) continue;
-          uint32_t u = __builtin_bit_cast(uint32_t, acc[i][j][r] * sr * rn[j]);
-          u += 0x7fffu + ((u >> 16) & 1u);
-          yrow[cols[j]] = static_cast<uint16_t>(u >> 16);
-        }
+        for (int j = 0; j < C::TJ; ++j)
+          if (cols[j] < a.m) yrow[cols[j]] = static_cast<__bf16>(acc[i][j][r] * sr * rn[j]);
       } else {
         float* yrow = reinterpret_cast<float*>(a.Y) + row * a.ldy;
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          if (!full && cols[j] >= a.m) continue;
-          yrow[cols[j]] = acc[i][j][r] * sr * rn[j];
-        }
+        for (int j = 0; j < C::TJ; ++j)
+          if (cols[j] < a.m) yrow[cols[j]] = acc[i][j][r] * sr * rn[j];
       }
     }
   }
@@ -328,21 +451,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_lut_gemm(GemmArgs a) {
 
 size_t lut_bytes(int bits) { return bits == 2 ? 256 * 8 : bits == 6 ? 4096 * 4 : 0; }
 
-template <int BA, int BW>
-hipError_t launch_bw(bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st) {
+template <int BA, int BW, int BM, int BN>
+hipError_t launch_cfg(bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st) {
   if (out_bf16)
-    hipLaunchKernelGGL((k_lut_gemm<BA, BW, true>), dim3(grid), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((k_lut_gemm<BA, BW, true, BM, BN>), dim3(grid), dim3(kThreads), lds, st, a);
   else
-    hipLaunchKernelGGL((k_lut_gemm<BA, BW, false>), dim3(grid), dim3(kThreads), lds, st, a);
+    hipLaunchKernelGGL((k_lut_gemm<BA, BW, false, BM, BN>), dim3(grid), dim3(kThreads), lds, st, a);
   return hipGetLastError();
 }
 
+template <int BA, int BW>
+hipError_t launch_bw(int cfg, bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st) {
+  return cfg == 0 ? launch_cfg<BA, BW, 384, 192>(out_bf16, a, grid, lds, st)
+                  : launch_cfg<BA, BW, 256, 256>(out_bf16, a, grid, lds, st);
+}
+
 template <int BA>
-hipError_t launch_ba(int bw, bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st) {
+hipError_t launch_ba(int bw, int cfg, bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st) {
   switch (bw) {
-    case 2: return launch_bw<BA, 2>(out_bf16, a, grid, lds, st);
-    case 4: return launch_bw<BA, 4>(out_bf16, a, grid, lds, st);
-    default: return launch_bw<BA, 6>(out_bf16, a, grid, lds, st);
+    case 2: return launch_bw<BA, 2>(cfg, out_bf16, a, grid, lds, st);
+    case 4: return launch_bw<BA, 4>(cfg, out_bf16, a, grid, lds, st);
+    default: return launch_bw<BA, 6>(cfg, out_bf16, a, grid, lds, st);
   }
 }
 
@@ -360,38 +489,83 @@ void tab4(const DecodeParams& dp, uint32_t* lt_lo, uint32_t* lt_hi, uint32_t* ht
   *ht_hi = h[1];
 }
 
+int device_cus() {
+  static thread_local int cached_dev = -1, cached_cus = 0;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 256;
+  if (dev != cached_dev) {
+    int cus = 0;
+    if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0) cus = 256;
+    cached_dev = dev;
+    cached_cus = cus;
+  }
+  return cached_cus;
+}
+
 }  // namespace
 
 int launch_lut_gemm(const uint8_t* x_codes, const float* x_norms, const DecodeParams& da, const uint8_t* w_codes,
                     const uint16_t* w_norms, const DecodeParams& dw, int64_t n, int64_t m, int64_t d, void* Y,
                     int y_bf16, int64_t ldy, hipStream_t stream) {
   GemmArgs a{};
-  a.xc = x_codes;
   a.xs = x_norms;
-  a.wc = w_codes;
   a.wn = w_norms;
-  a.Y = Y;
-  a.n = n;
-  a.m = m;
-  a.d = d;
   a.ldy = ldy;
-  a.xrow_bytes = d * da.bits / 8;
-  a.wrow_bytes = d * dw.bits / 8;
-  a.tiles_n = static_cast<int32_t>((n + BM - 1) / BM);
-  a.tiles_m = static_cast<int32_t>((m + BN - 1) / BN);
+  a.xrow_bytes = static_cast<int32_t>(d * da.bits / 8);
+  a.wrow_bytes = static_cast<int32_t>(d * dw.bits / 8);
+  a.nk = static_cast<int32_t>(d / KT);
   tab4(da, &a.lt_lo_a, &a.lt_hi_a, &a.ht_lo_a, &a.ht_hi_a);
   tab4(dw, &a.lt_lo_w, &a.lt_hi_w, &a.ht_lo_w, &a.ht_hi_w);
   for (int i = 0; i < 32; ++i) {
     a.mag_a[i] = da.mag[i];
     a.mag_w[i] = dw.mag[i];
   }
-  const int grid = a.tiles_n * a.tiles_m;
-  const size_t lds = 2 * (BM + BN) * KT * 2 + 128 + lut_bytes(da.bits) + lut_bytes(dw.bits);
-  hipError_t e;
-  switch (da.bits) {
-    case 2: e = launch_ba<2>(dw.bits, y_bf16 != 0, a, grid, lds, stream); break;
-    case 4: e = launch_ba<4>(dw.bits, y_bf16 != 0, a, grid, lds, stream); break;
-    default: e = launch_ba<6>(dw.bits, y_bf16 != 0, a, grid, lds, stream); break;
+  // tile shape: the one that leaves the least idle work when the tiles are dealt to the
+  // compute units in rounds (384 x 192 needs its LDS stages plus the tables to fit in 160 KB)
+  const int cus = device_cus();
+  const size_t luts = lut_bytes(da.bits) + lut_bytes(dw.bits);
+  int cfg = 1;
+  {
+    double best = 1e300;
+    for (int k = 0; k < 2; ++k) {
+      const int64_t bm = k == 0 ? 384 : 256, bn = k == 0 ? 192 : 256;
+      const size_t lds = (k == 0 ? Cfg<384, 192>::LDS : Cfg<256, 256>::LDS) + luts;
+      if (lds > 160 * 1024) continue;
+      const int64_t tiles = ((n + bm - 1) / bm) * ((m + bn - 1) / bn);
+      const int64_t rounds = (tiles + cus - 1) / cus;
+      const double cost = static_cast<double>(rounds) * bm * bn * (k == 0 ? 1.0 : 1.0001);
+      if (cost < best) {
+        best = cost;
+        cfg = k;
+      }
+    }
+  }
+  const int bm = cfg == 0 ? 384 : 256, bn = cfg == 0 ? 192 : 256;
+  const size_t lds = (cfg == 0 ? Cfg<384, 192>::LDS : Cfg<256, 256>::LDS) + luts;
+  // launches over row / column blocks keep every code extent addressable with 32-bit offsets
+  const int64_t max_rows_x = std::max<int64_t>(bm, (int64_t(1) << 31) / a.xrow_bytes / bm * bm);
+  const int64_t max_rows_w = std::max<int64_t>(bn, (int64_t(1) << 31) / a.wrow_bytes / bn * bn);
+  const int64_t esz = y_bf16 ? 2 : 4;
+  hipError_t e = hipSuccess;
+  for (int64_t r0 = 0; r0 < n && e == hipSuccess; r0 += max_rows_x) {
+    for (int64_t c0 = 0; c0 < m && e == hipSuccess; c0 += max_rows_w) {
+      GemmArgs b = a;
+      b.n = std::min(max_rows_x, n - r0);
+      b.m = std::min(max_rows_w, m - c0);
+      b.xc = x_codes + r0 * a.xrow_bytes;
+      b.xs = x_norms + r0;
+      b.wc = w_codes + c0 * a.wrow_bytes;
+      b.wn = w_norms + c0;
+      b.Y = static_cast<unsigned char*>(Y) + (r0 * ldy + c0) * esz;
+      b.tiles_n = static_cast<int32_t>((b.n + bm - 1) / bm);
+      b.tiles_m = static_cast<int32_t>((b.m + bn - 1) / bn);
+      const int grid = b.tiles_n * b.tiles_m;
+      switch (da.bits) {
+        case 2: e = launch_ba<2>(dw.bits, cfg, y_bf16 != 0, b, grid, lds, stream); break;
+        case 4: e = launch_ba<4>(dw.bits, cfg, y_bf16 != 0, b, grid, lds, stream); break;
+        default: e = launch_ba<6>(dw.bits, cfg, y_bf16 != 0, b, grid, lds, stream); break;
+      }
+    }
   }
   return static_cast<int>(e);
 }
