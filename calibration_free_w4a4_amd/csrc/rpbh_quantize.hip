@@ -12,12 +12,13 @@
 //     loops over token groups (persistent grid).
 //   * Staging: the lanes of a token load its bf16 row with coalesced 16-byte loads (lane q takes
 //     chunks q, q + L, q + 2L, q + 3L), prefetched one token group ahead in registers, store it
-//     to LDS and add the squares into a partial norm (sum of squares is invariant under Pi).
+//     to LDS and add the squares into a partial norm (sum of squares is invariant under Pi),
+//     reduced over aligned lane segments with DPP adds and across segments through LDS.
 //   * Compute: each lane gathers its 32 permuted positions x[perm[j]] from LDS with 16-bit reads
-//     (addresses precomputed once from perm), flips the Rademacher signs with one xor per bf16
-//     pair, and runs the block FWHT: the first butterfly stage and the bf16 -> fp32 widening
-//     with v_dot2_f32_bf16, the next four stages in registers, the last log2(h/32) stages across
-//     lanes with v_fmac_f32_dpp.
+//     (addresses precomputed once from perm) and runs the block FWHT: the Rademacher signs, the
+//     first butterfly stage and the bf16 -> fp32 widening are two v_dot2_f32_bf16 per bf16 pair
+//     against the pair's signs (the second with the high sign negated), the next four stages run
+//     in registers, the last log2(h/32) stages across lanes with v_fmac_f32_dpp.
 //   * Quantization uses the power-of-two-scaled coordinate t' = t * 2^k: one table lookup on
 //     floor(-t') and one fp32 compare give the exact nearest-centroid decision (QuantParams).
 //   * Codes are packed in registers and written with one 8/16/24-byte store per lane.
@@ -66,10 +67,6 @@ __device__ __forceinline__ float dot2_acc(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b),
-                                         0.0f, false);
-}
 
 // x[i] += sgn * (x[i] in the lane whose index differs in bit 0 / bit 1), for 8 registers, with
 // v_fmac_f32_dpp (one instruction per element).  The leading s_nop 4 covers the VALU-write ->
@@ -141,15 +138,40 @@ __device__ __forceinline__ uint32_t quantize_one(float tp, const float2* tbl, in
 }
 
 
-// bf16 pair dot product with a zero accumulator (VOP3P form, inline constant 0)
-__device__ __forceinline__ float dot2_zero(uint32_t a, uint32_t b) {
+
+// bf16 pair dot product with a zero accumulator, second operand in a VGPR (VOP3P form)
+__device__ __forceinline__ float dot2_v(uint32_t a, uint32_t b) {
   float r;
-  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "s"(b));
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
   return r;
 }
 
+// bf16 pair dot product with the high half of the second operand negated (VOP3P neg_hi)
+__device__ __forceinline__ float dot2_neghi(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+template <int CTRL, int ROWS>
+__device__ __forceinline__ float dpp_add(float x) {
+  return x + __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, ROWS, 0xF, false));
+}
+
+// Sum over aligned segments of `seg` lanes (a power of two <= 64, uniform); the last lane of
+// each segment holds the segment's sum (for seg <= 16 every lane does).
+__device__ __forceinline__ float segment_sum(float x, int seg) {
+  if (seg >= 2) x = dpp_add<0xB1, 0xF>(x);   // quad_perm [1,0,3,2]
+  if (seg >= 4) x = dpp_add<0x4E, 0xF>(x);   // quad_perm [2,3,0,1]
+  if (seg >= 8) x = dpp_add<0x141, 0xF>(x);  // row_half_mirror: 8 lanes
+  if (seg >= 16) x = dpp_add<0x140, 0xF>(x); // row_mirror: 16 lanes
+  if (seg >= 32) x = dpp_add<0x142, 0xA>(x); // row_bcast:15 into rows 1 and 3: 32 lanes
+  if (seg >= 64) x = dpp_add<0x143, 0xC>(x); // row_bcast:31 into rows 2 and 3: 64 lanes
+  return x;
+}
+
 template <int H, int BITS, QuantMode MODE>
-__global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
+__global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int d = a.d;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                                    // [tg][d]
@@ -178,7 +200,7 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
 
   // ---- set-up: gather addresses x[perm[j]] (LDS byte offsets) and sign masks of this lane
   uint32_t gaddr[kE];
-  uint32_t smask[kE / 2];
+  uint32_t smask[kE / 2];  // bf16 pairs (s_2i, s_2i+1) of the Rademacher signs
   {
     const int4* pp = reinterpret_cast<const int4*>(a.perm + j0);
     const uint32_t rowbase = static_cast<uint32_t>(slot * d);
@@ -194,9 +216,9 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
     const uint4 s0 = sp[0], s1 = sp[1];
     const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
 #pragma unroll
-    for (int i = 0; i < kE / 2; ++i) {  // int8 signs 2i, 2i+1 -> sign bits of a bf16 pair
+    for (int i = 0; i < kE / 2; ++i) {  // int8 signs 2i, 2i+1 -> bf16 (s_2i, s_2i+1)
       const uint32_t b = sw[i >> 1] >> (16 * (i & 1));
-      smask[i] = ((b & 0x80u) << 8) | ((b & 0x8000u) << 16);
+      smask[i] = 0x3F803F80u | ((b & 0x80u) << 8) | ((b & 0x8000u) << 16);
     }
   }
   // cross-lane butterflies leave the result negated in lanes with an odd number of "upper"
@@ -205,8 +227,6 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
   const float lane_sign = (__builtin_popcount(q & (LPB - 1)) & 1) ? -1.0f : 1.0f;
   const float sgn1 = (q & 1) ? -1.0f : 1.0f;
   const float sgn2 = (q & 2) ? -1.0f : 1.0f;
-  constexpr uint32_t kOnes = 0x3F803F80u;      // bf16 (1, 1)
-  constexpr uint32_t kPlusMinus = 0xBF803F80u; // bf16 (1, -1)
   uint4* stage_dst[4];
 #pragma unroll
   for (int c = 0; c < 4; ++c) stage_dst[c] = reinterpret_cast<uint4*>(xs + slot * d + 8 * (q + c * a.lpt));
@@ -240,8 +260,8 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
     }
     // prefetch the next group (the last iteration reloads its own group: no branch)
     load_group(g + static_cast<int>(gridDim.x) < a.ngroups ? g + static_cast<int>(gridDim.x) : g, v);
-    for (int off = 1; off < a.seg; off <<= 1) ss += __shfl_xor(ss, off, 64);
-    if (active && (q & (a.seg - 1)) == 0) part[slot * a.nseg + q / a.seg] = ss;
+    ss = segment_sum(ss, a.seg);
+    if (active && (q & (a.seg - 1)) == a.seg - 1) part[slot * a.nseg + q / a.seg] = ss;
     __syncthreads();
 
     // ---- gather the 32 permuted positions as bf16 pairs, signs, FWHT stage 1 (+ widening)
@@ -250,9 +270,9 @@ __global__ __launch_bounds__(512) void k_rpbh_quantize(QuantKernelArgs a) {
     for (int i = 0; i < kE / 2; ++i) {
       const uint32_t lo = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i]);
       const uint32_t hi = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i + 1]);
-      const uint32_t x2 = __builtin_amdgcn_perm(hi, lo, 0x05040100u) ^ smask[i];
-      y[2 * i] = dot2_zero(x2, kOnes);
-      y[2 * i + 1] = dot2_zero(x2, kPlusMinus);
+      const uint32_t x2 = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+      y[2 * i] = dot2_v(x2, smask[i]);
+      y[2 * i + 1] = dot2_neghi(x2, smask[i]);
     }
     // ---- FWHT stages 2..5 in registers
 #pragma unroll
