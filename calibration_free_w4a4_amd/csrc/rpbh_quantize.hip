@@ -104,28 +104,25 @@ __device__ __forceinline__ uint16_t bf16_rne_dev(float x) {
 }
 
 // Builds the per-bucket table: entry for bucket j = floor(-t') in [-J, J-1] is
-// (threshold, base code); the code is base + (|t'| > threshold).
+// (threshold, base code); the code is base + (|t'| > threshold).  The loop over the BITS-bit
+// codebook's positive boundaries is unrolled so that the thresholds are read from the kernel
+// arguments once (scalar loads with constant offsets), and the body has no branches.
+template <int BITS>
 __device__ void build_table(const QuantParams& qp, float2* tbl, int tid, int nthreads) {
-  const int J = qp.J, half = 1 << (qp.bits - 1);
+  constexpr int NB = (1 << (BITS - 1)) - 1, HALF = 1 << (BITS - 1);
+  const int J = qp.J;
   for (int e = tid; e < 2 * J; e += nthreads) {
     const int j = e - J;
+    const bool pos = j < 0;  // t' in (i, i + 1] with i = -j - 1; else |t'| in [j, j + 1), t' <= 0
+    const float lo = static_cast<float>(pos ? -j - 1 : j), hi = lo + 1.0f;
     float thr = __builtin_inff();
-    int base = 0;
-    if (j < 0) {  // t' in (i, i + 1], i = -j - 1
-      const float lo = static_cast<float>(-j - 1), hi = lo + 1.0f;
-      for (int p = 0; p < qp.nb; ++p) {
-        const float b = qp.thr_gt[p];
-        if (b <= lo) ++base;
-        else if (b < hi) thr = b;
-      }
-    } else {      // |t'| in [j, j + 1), t' <= 0
-      const float lo = static_cast<float>(j), hi = lo + 1.0f;
-      for (int p = 0; p < qp.nb; ++p) {
-        const float b = qp.thr_ge[p];
-        if (b < lo) ++base;
-        else if (b < hi) thr = b;
-      }
-      base += half;
+    int base = pos ? 0 : HALF;
+#pragma unroll
+    for (int p = 0; p < NB; ++p) {
+      const float b = pos ? qp.thr_gt[p] : qp.thr_ge[p];
+      const bool below = pos ? (b <= lo) : (b < lo);
+      base += below ? 1 : 0;
+      thr = (!below && b < hi) ? b : thr;
     }
     tbl[e] = make_float2(thr, __builtin_bit_cast(float, base));
   }
@@ -195,7 +192,7 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
   uint4 v[4];
   load_group(blockIdx.x, v);  // first group in flight during the set-up
 
-  if (MODE != QuantMode::kRotateOnly) build_table(a.qp, tbl_all, tid, blockDim.x);
+  if constexpr (MODE != QuantMode::kRotateOnly) build_table<BITS>(a.qp, tbl_all, tid, blockDim.x);
   const float2* tbl = tbl_all + J;
 
   // ---- set-up: gather addresses x[perm[j]] (LDS byte offsets) and sign masks of this lane
@@ -357,7 +354,11 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
 
 __global__ void k_quantize_t(const float* t, int64_t count, QuantParams qp, uint8_t* codes) {
   __shared__ float2 tbl_all[2 * kMaxTableHalf];
-  build_table(qp, tbl_all, threadIdx.x, blockDim.x);
+  switch (qp.bits) {
+    case 2: build_table<2>(qp, tbl_all, threadIdx.x, blockDim.x); break;
+    case 4: build_table<4>(qp, tbl_all, threadIdx.x, blockDim.x); break;
+    default: build_table<6>(qp, tbl_all, threadIdx.x, blockDim.x); break;
+  }
   __syncthreads();
   const float2* tbl = tbl_all + qp.J;
   for (int64_t i = blockIdx.x * static_cast<int64_t>(blockDim.x) + threadIdx.x; i < count;
