@@ -189,6 +189,25 @@ def test_lut_gemm_ragged(orbq, out_bf16):
     _gemm_case(orbq, 300, 520, 3072, 4, 4, out_bf16=out_bf16)
 
 
+@pytest.mark.parametrize("ba,bw", [(4, 4), (6, 4), (2, 6)])
+@pytest.mark.parametrize("d", [192, 320, 64])
+def test_lut_gemm_odd_k_tile_count(orbq, ba, bw, d):
+    """d / 64 odd: the kernel pads the K loop with a leading all-zero tile."""
+    assert _gemm_case(orbq, 70, 200, d, ba, bw) < 1e-5
+
+
+@pytest.mark.parametrize("ba,bw,out_bf16,d", [(4, 4, True, 512), (4, 4, False, 576), (6, 4, True, 512),
+                                               (4, 2, True, 576)])
+def test_lut_gemm_wide_tiles_ragged(orbq, ba, bw, out_bf16, d):
+    """Shapes for which the host picks 384 x 192 workgroup tiles, with partial tiles on both axes
+    (last token tile 284 of 384 rows, last weight tile 136 of 192 rows) and even or odd K-tile
+    counts; sampled outputs include the ragged borders."""
+    n, m = 4508, 12232  # Y rows stay 16-byte aligned (m multiple of 8)
+    ii = np.unique(np.concatenate([np.arange(0, 40), np.arange(4224 - 8, 4224 + 8), np.arange(n - 40, n)]))
+    jj = np.unique(np.concatenate([np.arange(0, 40), np.arange(12096 - 8, 12096 + 8), np.arange(m - 40, m)]))
+    _gemm_case(orbq, n, m, d, ba, bw, out_bf16=out_bf16, sample=(ii, jj))
+
+
 def test_lut_gemm_from_oracle_codes(orbq):
     """The product of codes the oracle produced from real activations and weights."""
     torch = torch_mod()
