@@ -7,21 +7,23 @@
 // kernel folds weight rows ("Offline Weight Quantization") with bf16 norms.
 //
 // Work layout (gfx950, wave64):
-//   * 32 consecutive post-permutation positions of one token per lane; a Hadamard block of
-//     h = 128 spans one quad of lanes (h = 64: a lane pair).  A workgroup holds `tg` tokens and
-//     loops over token groups (persistent grid).
+//   * 16 post-permutation positions of one token per lane; a Hadamard block of h = 128 spans 8
+//     lanes (h = 64: 4 lanes).  A workgroup holds `tg` tokens (up to 1024 threads) and loops over
+//     token groups (persistent grid sized by the kernel's occupancy).  Short rows per lane keep the
+//     registers at ~80, so six waves share each SIMD and hide the load / LDS / barrier latencies.
 //   * Staging: the lanes of a token load its bf16 row with coalesced 16-byte loads (lane q takes
-//     chunks q, q + L, q + 2L, q + 3L), prefetched one token group ahead in registers, store it
-//     to LDS and add the squares into a partial norm (sum of squares is invariant under Pi),
-//     reduced over aligned lane segments with DPP adds and across segments through LDS.
-//   * Compute: each lane gathers its 32 permuted positions x[perm[j]] from LDS with 16-bit reads
+//     chunks q and q + L), prefetched one token group ahead in registers, store it to LDS and add
+//     the squares into a partial norm (sum of squares is invariant under Pi), reduced over aligned
+//     lane segments with DPP adds and across segments through LDS.
+//   * Compute: each lane gathers its 16 permuted positions x[perm[j]] from LDS with 16-bit reads
 //     (addresses precomputed once from perm) and runs the block FWHT: the Rademacher signs, the
 //     first butterfly stage and the bf16 -> fp32 widening are two v_dot2_f32_bf16 per bf16 pair
-//     against the pair's signs (the second with the high sign negated), the next four stages run
-//     in registers, the last log2(h/32) stages across lanes with v_fmac_f32_dpp.
+//     against the pair's signs (the second with the high sign negated), the next three stages
+//     run in registers, the last log2(h/16) stages across lanes with v_fmac_f32_dpp (lanes placed
+//     so that every partner is a quad_perm or row_half_mirror lane).
 //   * Quantization uses the power-of-two-scaled coordinate t' = t * 2^k: one table lookup on
 //     floor(-t') and one fp32 compare give the exact nearest-centroid decision (QuantParams).
-//   * Codes are packed in registers and written with one 8/16/24-byte store per lane.
+//   * Codes are packed in registers and written with one 4/8/12-byte store per lane.
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -35,7 +37,8 @@ namespace {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef unsigned short u16x2_t __attribute__((ext_vector_type(2)));
 
-constexpr int kE = 32;  // positions per lane
+constexpr int kE = 16;  // positions per lane
+constexpr int kCH = kE / 8;  // 16-byte input chunks staged per lane
 
 struct QuantKernelArgs {
   const uint16_t* X;
@@ -168,7 +171,7 @@ __device__ __forceinline__ float segment_sum(float x, int seg) {
 }
 
 template <int H, int BITS, QuantMode MODE>
-__global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
+__global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int d = a.d;
   uint16_t* xs = reinterpret_cast<uint16_t*>(smem);                                    // [tg][d]
@@ -180,16 +183,24 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
   const int slot = active ? tid / a.lpt : 0;
   const int q = active ? tid - slot * a.lpt : 0;
   const int J = a.qp.J;
-  const int j0 = kE * q;
+  // Lane -> positions: a Hadamard block of h = 128 spans 8 consecutive lanes, lane i of the 8
+  // holding the 16 positions 16 b .. 16 b + 15 with b = i (i < 4) or 11 - i (i >= 4), so that
+  // the partners of the three cross-lane butterfly stages (b xor 1, b xor 2, b xor 4) are the
+  // DPP quad_perm [1,0,3,2], quad_perm [2,3,0,1] and row_half_mirror lanes.  h = 64 spans 4
+  // lanes in natural order.
+  constexpr int LPB = H / kE;  // lanes per Hadamard block
+  const int li = q & (LPB - 1);
+  const int bl = (LPB == 8 && li >= 4) ? 11 - li : li;
+  const int j0 = H * (q / LPB) + kE * bl;
 
   // rows past the end (and idle lanes) load a valid row and store nothing
-  auto load_group = [&](int g, uint4 v[4]) {
+  auto load_group = [&](int g, uint4 v[kCH]) {
     const int64_t row = min(static_cast<int64_t>(g) * a.tg + slot, a.n - 1);
     const uint16_t* src = a.X + row * a.ldx;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = *reinterpret_cast<const uint4*>(src + 8 * (q + c * a.lpt));
+    for (int c = 0; c < kCH; ++c) v[c] = *reinterpret_cast<const uint4*>(src + 8 * (q + c * a.lpt));
   };
-  uint4 v[4];
+  uint4 v[kCH];
   load_group(blockIdx.x, v);  // first group in flight during the set-up
 
   if constexpr (MODE != QuantMode::kRotateOnly) build_table<BITS>(a.qp, tbl_all, tid, blockDim.x);
@@ -209,9 +220,8 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
       for (int e = 0; e < 4; ++e)
         gaddr[4 * c + e] = (rowbase + static_cast<uint32_t>(min(max(pv[e], 0), d - 1))) * 2u;
     }
-    const uint4* sp = reinterpret_cast<const uint4*>(a.signs + j0);
-    const uint4 s0 = sp[0], s1 = sp[1];
-    const uint32_t sw[8] = {s0.x, s0.y, s0.z, s0.w, s1.x, s1.y, s1.z, s1.w};
+    const uint4 s0 = *reinterpret_cast<const uint4*>(a.signs + j0);  // kE = 16 signs
+    const uint32_t sw[4] = {s0.x, s0.y, s0.z, s0.w};
 #pragma unroll
     for (int i = 0; i < kE / 2; ++i) {  // int8 signs 2i, 2i+1 -> bf16 (s_2i, s_2i+1)
       const uint32_t b = sw[i >> 1] >> (16 * (i & 1));
@@ -220,13 +230,13 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
   }
   // cross-lane butterflies leave the result negated in lanes with an odd number of "upper"
   // positions; fold that sign into the per-token scale
-  constexpr int LPB = H / kE;  // lanes per Hadamard block
-  const float lane_sign = (__builtin_popcount(q & (LPB - 1)) & 1) ? -1.0f : 1.0f;
-  const float sgn1 = (q & 1) ? -1.0f : 1.0f;
-  const float sgn2 = (q & 2) ? -1.0f : 1.0f;
-  uint4* stage_dst[4];
+  const float lane_sign = (__builtin_popcount(bl) & 1) ? -1.0f : 1.0f;
+  const float sgn1 = (bl & 1) ? -1.0f : 1.0f;
+  const float sgn2 = (bl & 2) ? -1.0f : 1.0f;
+  const float sgn3 = (bl & 4) ? -1.0f : 1.0f;
+  uint4* stage_dst[kCH];
 #pragma unroll
-  for (int c = 0; c < 4; ++c) stage_dst[c] = reinterpret_cast<uint4*>(xs + slot * d + 8 * (q + c * a.lpt));
+  for (int c = 0; c < kCH; ++c) stage_dst[c] = reinterpret_cast<uint4*>(xs + slot * d + 8 * (q + c * a.lpt));
 
   // Stores go through buffer resources: lanes with nothing to store (rows past the end, idle
   // lanes) get an offset past the extent and the hardware drops the store.  The loop body has no
@@ -242,14 +252,14 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
     const bool valid = active && row < a.n;
 
     __syncthreads();  // the previous group's gathers from xs are done
-    // ---- stage this lane's 4 chunks; partial sum of squares
+    // ---- stage this lane's chunks; partial sum of squares
     float ss = 0.0f;
     if (active) {
 #pragma unroll
-      for (int c = 0; c < 4; ++c) *stage_dst[c] = v[c];
+      for (int c = 0; c < kCH; ++c) *stage_dst[c] = v[c];
     }
 #pragma unroll
-    for (int c = 0; c < 4; ++c) {
+    for (int c = 0; c < kCH; ++c) {
       ss = dot2_acc(v[c].x, v[c].x, ss);
       ss = dot2_acc(v[c].y, v[c].y, ss);
       ss = dot2_acc(v[c].z, v[c].z, ss);
@@ -286,14 +296,14 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
     if constexpr (LPB >= 2) {
       ORBQ_DPP_FMAC8("quad_perm:[1,0,3,2]", y, sgn1);
       ORBQ_DPP_FMAC8("quad_perm:[1,0,3,2]", y + 8, sgn1);
-      ORBQ_DPP_FMAC8("quad_perm:[1,0,3,2]", y + 16, sgn1);
-      ORBQ_DPP_FMAC8("quad_perm:[1,0,3,2]", y + 24, sgn1);
     }
     if constexpr (LPB >= 4) {
       ORBQ_DPP_FMAC8("quad_perm:[2,3,0,1]", y, sgn2);
       ORBQ_DPP_FMAC8("quad_perm:[2,3,0,1]", y + 8, sgn2);
-      ORBQ_DPP_FMAC8("quad_perm:[2,3,0,1]", y + 16, sgn2);
-      ORBQ_DPP_FMAC8("quad_perm:[2,3,0,1]", y + 24, sgn2);
+    }
+    if constexpr (LPB >= 8) {
+      ORBQ_DPP_FMAC8("row_half_mirror", y, sgn3);
+      ORBQ_DPP_FMAC8("row_half_mirror", y + 8, sgn3);
     }
 
     // ---- token norm: the lane segments' partial sums, added in a fixed order
@@ -304,7 +314,7 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
 
     if constexpr (MODE == QuantMode::kRotateOnly) {
       const float sc = a.inv_scale * lane_sign;
-      const uint32_t off = valid ? (lane_row * static_cast<uint32_t>(d) + kE * q) * 4u : kDropped;
+      const uint32_t off = valid ? (lane_row * static_cast<uint32_t>(d) + j0) * 4u : kDropped;
 #pragma unroll
       for (int c = 0; c < kE / 4; ++c) {
         const v4i_t w = {__builtin_bit_cast(int, y[4 * c] * sc), __builtin_bit_cast(int, y[4 * c + 1] * sc),
@@ -315,21 +325,20 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
                                             (valid && q == 0) ? lane_row * 4u : kDropped, 0, 0);
     } else {
       const float inv_s = lane_sign * (a.inv_scale / (s + a.eps));
-      const uint32_t off = valid ? lane_row * row_bytes + q * (kE * BITS / 8) : kDropped;
+      const uint32_t off = valid ? lane_row * row_bytes + static_cast<uint32_t>(j0 * BITS / 8) : kDropped;
       if constexpr (BITS == 4) {
-        uint32_t w[4] = {0, 0, 0, 0};
-#pragma unroll
-        for (int i = 0; i < kE; ++i) w[i >> 3] |= quantize_one(y[i] * inv_s, tbl, J) << (4 * (i & 7));
-        const v4i_t wv = {static_cast<int>(w[0]), static_cast<int>(w[1]), static_cast<int>(w[2]), static_cast<int>(w[3])};
-        __builtin_amdgcn_raw_buffer_store_b128(wv, codes_rs, off, 0, 0);
-      } else if constexpr (BITS == 2) {
         uint32_t w[2] = {0, 0};
 #pragma unroll
-        for (int i = 0; i < kE; ++i) w[i >> 4] |= quantize_one(y[i] * inv_s, tbl, J) << (2 * (i & 15));
+        for (int i = 0; i < kE; ++i) w[i >> 3] |= quantize_one(y[i] * inv_s, tbl, J) << (4 * (i & 7));
         const v2u_t wv = {w[0], w[1]};
         __builtin_amdgcn_raw_buffer_store_b64(wv, codes_rs, off, 0, 0);
+      } else if constexpr (BITS == 2) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int i = 0; i < kE; ++i) w |= quantize_one(y[i] * inv_s, tbl, J) << (2 * i);
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(w), codes_rs, off, 0, 0);
       } else {
-        uint32_t w[6] = {0, 0, 0, 0, 0, 0};
+        uint32_t w[3] = {0, 0, 0};
 #pragma unroll
         for (int i = 0; i < kE; ++i) {
           const uint32_t c = quantize_one(y[i] * inv_s, tbl, J);
@@ -337,10 +346,9 @@ __global__ __launch_bounds__(512, 4) void k_rpbh_quantize(QuantKernelArgs a) {
           w[wi] |= c << sh;
           if (sh > 26) w[wi + 1] |= c >> (32 - sh);
         }
-        const v2u_t w0 = {w[0], w[1]}, w1 = {w[2], w[3]}, w2 = {w[4], w[5]};
-        __builtin_amdgcn_raw_buffer_store_b64(w0, codes_rs, off, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(w1, codes_rs, off + 8u, 0, 0);
-        __builtin_amdgcn_raw_buffer_store_b64(w2, codes_rs, off + 16u, 0, 0);
+        const v2u_t w01 = {w[0], w[1]};
+        __builtin_amdgcn_raw_buffer_store_b64(w01, codes_rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(w[2]), codes_rs, off + 8u, 0, 0);
       }
       if constexpr (MODE == QuantMode::kWeights)
         __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(bf16_rne_dev(s)), norms_rs,
@@ -366,26 +374,42 @@ __global__ void k_quantize_t(const float* t, int64_t count, QuantParams qp, uint
     codes[i] = static_cast<uint8_t>(quantize_one(t[i] * qp.scale, tbl, qp.J));
 }
 
+int device_cu_count();
+
+// Balanced persistent grid: every workgroup runs the same number of token groups, and all of
+// them are resident at once (as many workgroups per CU as the kernel's occupancy allows).
 template <int H, int BITS, QuantMode MODE>
-hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, int grid, hipStream_t st) {
+hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
+  static thread_local int cached_threads = -1, cached_occ = 1;
+  static thread_local size_t cached_lds = 0;
+  if (threads != cached_threads || lds != cached_lds) {
+    int occ = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_rpbh_quantize<H, BITS, MODE>, threads, lds) != hipSuccess ||
+        occ < 1)
+      occ = 1;
+    cached_threads = threads;
+    cached_lds = lds;
+    cached_occ = occ;
+  }
+  const int max_grid = device_cu_count() * cached_occ;
+  const int iters = (a.ngroups + max_grid - 1) / max_grid;
+  const int grid = (a.ngroups + iters - 1) / iters;
   hipLaunchKernelGGL((k_rpbh_quantize<H, BITS, MODE>), dim3(grid), dim3(threads), lds, st, a);
   return hipGetLastError();
 }
 
 template <int H, QuantMode MODE>
-hipError_t launch_bits(int bits, const QuantKernelArgs& a, int threads, size_t lds, int grid, hipStream_t st) {
+hipError_t launch_bits(int bits, const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
   switch (bits) {
-    case 2: return launch_typed<H, 2, MODE>(a, threads, lds, grid, st);
-    case 4: return launch_typed<H, 4, MODE>(a, threads, lds, grid, st);
-    default: return launch_typed<H, 6, MODE>(a, threads, lds, grid, st);
+    case 2: return launch_typed<H, 2, MODE>(a, threads, lds, st);
+    case 4: return launch_typed<H, 4, MODE>(a, threads, lds, st);
+    default: return launch_typed<H, 6, MODE>(a, threads, lds, st);
   }
 }
 
 template <QuantMode MODE>
-hipError_t launch_mode(int block, int bits, const QuantKernelArgs& a, int threads, size_t lds, int grid,
-                       hipStream_t st) {
-  return block == 64 ? launch_bits<64, MODE>(bits, a, threads, lds, grid, st)
-                     : launch_bits<128, MODE>(bits, a, threads, lds, grid, st);
+hipError_t launch_mode(int block, int bits, const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
+  return block == 64 ? launch_bits<64, MODE>(bits, a, threads, lds, st) : launch_bits<128, MODE>(bits, a, threads, lds, st);
 }
 
 int device_cu_count() {
@@ -426,7 +450,7 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
   // tokens per workgroup: least idle lanes, then the workgroup closest to 256 threads
   int best_tg = 1, best_threads = 0;
   double best_score = 1e30;
-  for (int tg = 1; tg * a.lpt <= 512; ++tg) {
+  for (int tg = 1; tg * a.lpt <= 1024; ++tg) {
     const int act = tg * a.lpt, thr = (act + 63) / 64 * 64;
     const double waste = static_cast<double>(thr - act) / thr;
     const double score = waste * 10.0 + std::abs(std::log2(thr / 256.0)) * 0.01;
@@ -465,21 +489,15 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
     if (x_rot) c.x_rot = x_rot + r0 * rot.d;
     c.rot_bytes = x_rot ? static_cast<uint32_t>(rows * rot.d * 4) : 0u;
     c.ngroups = static_cast<int>((rows + a.tg - 1) / a.tg);
-    // balanced persistent grid: every workgroup runs the same number of token groups, and all of
-    // them fit on the chip at once (4 waves per SIMD at <= 128 VGPRs)
-    const int waves_per_wg = best_threads / 64;
-    const int max_grid = device_cu_count() * std::max(1, 16 / waves_per_wg);
-    const int iters = (c.ngroups + max_grid - 1) / max_grid;
-    const int grid = (c.ngroups + iters - 1) / iters;
     switch (mode) {
       case QuantMode::kActivations:
-        e = launch_mode<QuantMode::kActivations>(rot.block, bits, c, best_threads, lds, grid, stream);
+        e = launch_mode<QuantMode::kActivations>(rot.block, bits, c, best_threads, lds, stream);
         break;
       case QuantMode::kWeights:
-        e = launch_mode<QuantMode::kWeights>(rot.block, bits, c, best_threads, lds, grid, stream);
+        e = launch_mode<QuantMode::kWeights>(rot.block, bits, c, best_threads, lds, stream);
         break;
       default:
-        e = launch_mode<QuantMode::kRotateOnly>(rot.block, 4, c, best_threads, lds, grid, stream);
+        e = launch_mode<QuantMode::kRotateOnly>(rot.block, 4, c, best_threads, lds, stream);
         break;
     }
   }
