@@ -149,21 +149,22 @@ def main() -> int:
         gemm()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, HIP events around each kernel on the launch stream
-    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    # ---- timed region: K steps, HIP events on the launch stream before each kernel (a step's
+    # first event also ends the previous step's lut_gemm), one more after the last step
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(args.steps):
-        ev[k][0].record()
+        ev[2 * k].record()
         quantize()
-        ev[k][1].record()
+        ev[2 * k + 1].record()
         gemm()
-        ev[k][2].record()
+    ev[2 * args.steps].record()
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_step = (t1 - t0) * 1e3 / args.steps
-    q_ms = statistics.mean(e[0].elapsed_time(e[1]) for e in ev)
-    g_ms = statistics.mean(e[1].elapsed_time(e[2]) for e in ev)
+    q_ms = statistics.mean(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps))
+    g_ms = statistics.mean(ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps))
 
     flops = L.flops
     q_bytes = L.n * (2 * L.d + L.d * L.bits_a // 8 + 4)
