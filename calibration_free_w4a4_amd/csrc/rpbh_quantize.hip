@@ -58,6 +58,7 @@ struct QuantKernelArgs {
   float eps;
   float inv_scale; // 2^k / sqrt(h) (quantize) or 1 / sqrt(h) (rotate only)
   uint32_t codes_bytes, norms_bytes, rot_bytes;  // buffer extents (< 2^31) for bounds-dropped stores
+  uint32_t x_bytes;                              // extent of X in this launch (< 2^31)
   QuantParams qp;
 };
 
@@ -193,12 +194,17 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
   const int bl = (LPB == 8 && li >= 4) ? 11 - li : li;
   const int j0 = H * (q / LPB) + kE * bl;
 
-  // rows past the end (and idle lanes) load a valid row and store nothing
+  // X is read through a buffer resource that ends at the last row of the launch: rows past the
+  // end read as zero (and are never stored); idle lanes read the group's first row
+  const __amdgpu_buffer_rsrc_t x_rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(a.X), 0, a.x_bytes, kBufWord3);
+  const uint32_t ldx_bytes = static_cast<uint32_t>(a.ldx) * 2u;
+  const uint32_t lane_off = static_cast<uint32_t>(16 * q);
   auto load_group = [&](int g, uint4 v[kCH]) {
-    const int64_t row = min(static_cast<int64_t>(g) * a.tg + slot, a.n - 1);
-    const uint16_t* src = a.X + row * a.ldx;
+    const uint32_t off = (static_cast<uint32_t>(g) * static_cast<uint32_t>(a.tg) + slot) * ldx_bytes + lane_off;
 #pragma unroll
-    for (int c = 0; c < kCH; ++c) v[c] = *reinterpret_cast<const uint4*>(src + 8 * (q + c * a.lpt));
+    for (int c = 0; c < kCH; ++c)
+      v[c] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(x_rs, off + static_cast<uint32_t>(c * 16 * a.lpt), 0, 0));
   };
   uint4 v[kCH];
   load_group(blockIdx.x, v);  // first group in flight during the set-up
@@ -309,7 +315,9 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
     // ---- token norm: the lane segments' partial sums, added in a fixed order
     float s2 = 0.0f;
     for (int k = 0; k < a.nseg; ++k) s2 += part[slot * a.nseg + k];
-    const float s = __builtin_sqrtf(s2);
+    // hardware square root and reciprocal (1 ulp): s is reported to fp32 accuracy and t' only
+    // needs fp32 accuracy; the correctly rounded forms cost ~20 instructions per lane
+    const float s = __builtin_amdgcn_sqrtf(s2);
     const uint32_t lane_row = static_cast<uint32_t>(row);  // < n < 2^31 within a launch chunk
 
     if constexpr (MODE == QuantMode::kRotateOnly) {
@@ -324,7 +332,7 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, s), norms_rs,
                                             (valid && q == 0) ? lane_row * 4u : kDropped, 0, 0);
     } else {
-      const float inv_s = lane_sign * (a.inv_scale / (s + a.eps));
+      const float inv_s = lane_sign * a.inv_scale * __builtin_amdgcn_rcpf(s + a.eps);
       const uint32_t off = valid ? lane_row * row_bytes + static_cast<uint32_t>(j0 * BITS / 8) : kDropped;
       if constexpr (BITS == 4) {
         uint32_t w[2] = {0, 0};
@@ -470,8 +478,8 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
                                                                                  std::sqrt(static_cast<double>(rot.block)));
   const size_t lds = ((static_cast<size_t>(a.tg) * rot.d * 2 + 15) & ~size_t(15)) +
                      sizeof(float2) * 2 * a.qp.J + sizeof(float) * a.tg * a.nseg;
-  // rows per launch: every buffer extent (codes, norms, rotated rows) stays below 2^31 bytes
-  const int64_t bytes_per_row = std::max<int64_t>(rot.d * 4, rot.d);
+  // rows per launch: every buffer extent (input rows, codes, norms, rotated rows) stays below 2^31 bytes
+  const int64_t bytes_per_row = std::max<int64_t>(std::max<int64_t>(rot.d * 4, rot.d), ldx * 2);
   const int64_t chunk_rows = std::max<int64_t>(a.tg, ((int64_t(1) << 31) - 4096) / bytes_per_row / a.tg * a.tg);
   hipError_t e = hipSuccess;
   const int bits = a.qp.bits;
@@ -480,6 +488,7 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
     const int64_t rows = std::min<int64_t>(chunk_rows, n - r0);
     c.n = rows;
     c.X = X + r0 * ldx;
+    c.x_bytes = static_cast<uint32_t>((rows - 1) * ldx * 2 + static_cast<int64_t>(rot.d) * 2);
     const int64_t cb = static_cast<int64_t>(rot.d) * (mode == QuantMode::kRotateOnly ? 4 : a.qp.bits) / 8;
     if (codes) c.codes = codes + r0 * cb;
     c.codes_bytes = static_cast<uint32_t>(rows * cb);
