@@ -117,23 +117,27 @@ def _dev_tensor(t, dtype, name):
 # ---------------------------------------------------------------- descriptors
 @dataclass
 class Rotation:
-    """RPBH rotation for dimension d: device perm (int32[d]) and signs (int8[d])."""
+    """RPBH rotation for dimension d: device perm (int32[d], or None for the identity) and
+    signs (int8[d])."""
     d: int
     block: int
     perm: "object"
     signs: "object"
 
     @classmethod
-    def create(cls, d: int, block: int, perm: np.ndarray, signs: np.ndarray, device=None) -> "Rotation":
-        perm = np.ascontiguousarray(perm, dtype=np.int32)
+    def create(cls, d: int, block: int, perm, signs: np.ndarray, device=None) -> "Rotation":
         signs = np.ascontiguousarray(signs, dtype=np.int8)
-        _check(load().orbq_rpbh_validate(d, block, perm.ctypes.data, signs.ctypes.data), "orbq_rpbh_validate")
+        if perm is not None:
+            perm = np.ascontiguousarray(perm, dtype=np.int32)
+        _check(load().orbq_rpbh_validate(d, block, None if perm is None else perm.ctypes.data, signs.ctypes.data),
+               "orbq_rpbh_validate")
         torch = _torch()
         dev = device or torch.device("cuda", torch.cuda.current_device())
-        return cls(d, block, torch.from_numpy(perm).to(dev), torch.from_numpy(signs).to(dev))
+        dperm = None if perm is None else torch.from_numpy(perm).to(dev)
+        return cls(d, block, dperm, torch.from_numpy(signs).to(dev))
 
     def struct(self) -> _Rpbh:
-        return _Rpbh(self.d, self.block, self.perm.data_ptr(), self.signs.data_ptr())
+        return _Rpbh(self.d, self.block, 0 if self.perm is None else self.perm.data_ptr(), self.signs.data_ptr())
 
 
 @dataclass

@@ -53,12 +53,12 @@ int check_codebook(const orbq_codebook* cb, int64_t d, const char* what) {
 
 int check_rot(const orbq_rpbh* rot, int64_t d, const char* what) {
   if (!rot) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation is NULL", what);
-  if (!rot->perm || !rot->signs) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation arrays are NULL", what);
+  if (!rot->signs) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation signs are NULL", what);
   if (rot->d != d) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation d=%d but d=%lld", what, rot->d, (long long)d);
-  if (rot->block != 64 && rot->block != 128)
-    return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not in {64,128}", what, rot->block);
+  if (rot->block < 64 || rot->block > 1024 || (rot->block & (rot->block - 1)))
+    return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not a power of two in [64, 1024]", what, rot->block);
   if (d % rot->block) return fail(ORBQ_ERR_INVALID_ARG, "%s: d=%lld not a multiple of block %d", what, (long long)d, rot->block);
-  if (!aligned(rot->perm, 16) || !aligned(rot->signs, 16))
+  if ((rot->perm && !aligned(rot->perm, 16)) || !aligned(rot->signs, 16))
     return fail(ORBQ_ERR_ALIGNMENT, "%s: rotation arrays must be 16-byte aligned", what);
   return ORBQ_OK;
 }
@@ -117,15 +117,19 @@ ORBQ_API int orbq_codebook_lloyd_max(int32_t d, int32_t bits, float* centroids_o
 
 ORBQ_API int orbq_rpbh_validate(int32_t d, int32_t block, const int32_t* perm, const int8_t* signs) {
   const char* what = "orbq_rpbh_validate";
-  if (!perm || !signs) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL array", what);
+  if (!signs) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL signs", what);
   int s;
   if ((s = check_dim(d, what))) return s;
-  if (block != 64 && block != 128) return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not in {64,128}", what, block);
+  if (block < 64 || block > 1024 || (block & (block - 1)))
+    return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not a power of two in [64, 1024]", what, block);
   if (d % block) return fail(ORBQ_ERR_INVALID_ARG, "%s: d not a multiple of block", what);
   std::vector<unsigned char> seen(d, 0);
   for (int j = 0; j < d; ++j) {
-    if (perm[j] < 0 || perm[j] >= d || seen[perm[j]]) return fail(ORBQ_ERR_INVALID_ARG, "%s: perm is not a permutation (entry %d)", what, j);
-    seen[perm[j]] = 1;
+    if (perm) {
+      if (perm[j] < 0 || perm[j] >= d || seen[perm[j]])
+        return fail(ORBQ_ERR_INVALID_ARG, "%s: perm is not a permutation (entry %d)", what, j);
+      seen[perm[j]] = 1;
+    }
     if (signs[j] != 1 && signs[j] != -1) return fail(ORBQ_ERR_INVALID_ARG, "%s: sign %d is not +-1", what, j);
   }
   return ok();

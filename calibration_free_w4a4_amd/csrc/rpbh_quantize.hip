@@ -171,7 +171,7 @@ __device__ __forceinline__ float segment_sum(float x, int seg) {
   return x;
 }
 
-template <int H, int BITS, QuantMode MODE>
+template <int H, int BITS, QuantMode MODE, bool PERM>
 __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int d = a.d;
@@ -184,14 +184,15 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
   const int slot = active ? tid / a.lpt : 0;
   const int q = active ? tid - slot * a.lpt : 0;
   const int J = a.qp.J;
-  // Lane -> positions: a Hadamard block of h = 128 spans 8 consecutive lanes, lane i of the 8
-  // holding the 16 positions 16 b .. 16 b + 15 with b = i (i < 4) or 11 - i (i >= 4), so that
-  // the partners of the three cross-lane butterfly stages (b xor 1, b xor 2, b xor 4) are the
-  // DPP quad_perm [1,0,3,2], quad_perm [2,3,0,1] and row_half_mirror lanes.  h = 64 spans 4
-  // lanes in natural order.
-  constexpr int LPB = H / kE;  // lanes per Hadamard block
+  // Lane -> positions: a Hadamard block of h spans h / 16 consecutive lanes; lane i of a block
+  // holds the 16 positions 16 b .. 16 b + 15 of the block with b = M i over GF(2):
+  //   b0 = i0 ^ i2,  b1 = i1 ^ i2,  b2 = i2 ^ i3,  b3 = i3,  b4 = i4,  b5 = i5,
+  // so that the partners of the cross-lane butterfly stages b xor 1, 2, 4, 8 are the DPP
+  // quad_perm [1,0,3,2], quad_perm [2,3,0,1], row_half_mirror (i xor 7) and row_mirror
+  // (i xor 15) lanes, and b xor 16, 32 the lanes i xor 16 (ds_swizzle) and i xor 32.
+  constexpr int LPB = H / kE;  // lanes per Hadamard block (4 .. 64)
   const int li = q & (LPB - 1);
-  const int bl = (LPB == 8 && li >= 4) ? 11 - li : li;
+  const int bl = li ^ (((li >> 2) & 1) * 3) ^ (((li >> 3) & 1) * 4);
   const int j0 = H * (q / LPB) + kE * bl;
 
   // X is read through a buffer resource that ends at the last row of the launch: rows past the
@@ -216,6 +217,7 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
   uint32_t gaddr[kE];
   uint32_t smask[kE / 2];  // bf16 pairs (s_2i, s_2i+1) of the Rademacher signs
   {
+    if constexpr (PERM) {
     const int4* pp = reinterpret_cast<const int4*>(a.perm + j0);
     const uint32_t rowbase = static_cast<uint32_t>(slot * d);
 #pragma unroll
@@ -225,6 +227,10 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
 #pragma unroll
       for (int e = 0; e < 4; ++e)
         gaddr[4 * c + e] = (rowbase + static_cast<uint32_t>(min(max(pv[e], 0), d - 1))) * 2u;
+    }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kE; ++e) gaddr[e] = 0u;
     }
     const uint4 s0 = *reinterpret_cast<const uint4*>(a.signs + j0);  // kE = 16 signs
     const uint32_t sw[4] = {s0.x, s0.y, s0.z, s0.w};
@@ -240,6 +246,9 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
   const float sgn1 = (bl & 1) ? -1.0f : 1.0f;
   const float sgn2 = (bl & 2) ? -1.0f : 1.0f;
   const float sgn3 = (bl & 4) ? -1.0f : 1.0f;
+  const float sgn4 = (bl & 8) ? -1.0f : 1.0f;
+  const float sgn5 = (bl & 16) ? -1.0f : 1.0f;
+  const float sgn6 = (bl & 32) ? -1.0f : 1.0f;
   uint4* stage_dst[kCH];
 #pragma unroll
   for (int c = 0; c < kCH; ++c) stage_dst[c] = reinterpret_cast<uint4*>(xs + slot * d + 8 * (q + c * a.lpt));
@@ -279,13 +288,24 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
 
     // ---- gather the 32 permuted positions as bf16 pairs, signs, FWHT stage 1 (+ widening)
     float y[kE];
+    if constexpr (PERM) {
 #pragma unroll
-    for (int i = 0; i < kE / 2; ++i) {
-      const uint32_t lo = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i]);
-      const uint32_t hi = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i + 1]);
-      const uint32_t x2 = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
-      y[2 * i] = dot2_v(x2, smask[i]);
-      y[2 * i + 1] = dot2_neghi(x2, smask[i]);
+      for (int i = 0; i < kE / 2; ++i) {
+        const uint32_t lo = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i]);
+        const uint32_t hi = *reinterpret_cast<const uint16_t*>(smem + gaddr[2 * i + 1]);
+        const uint32_t x2 = __builtin_amdgcn_perm(hi, lo, 0x05040100u);
+        y[2 * i] = dot2_v(x2, smask[i]);
+        y[2 * i + 1] = dot2_neghi(x2, smask[i]);
+      }
+    } else {  // identity permutation (block RHT): the lane's 16 positions are contiguous
+      const uint4* src = reinterpret_cast<const uint4*>(xs + slot * d + j0);
+      const uint4 c0 = src[0], c1 = src[1];
+      const uint32_t x2s[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
+#pragma unroll
+      for (int i = 0; i < kE / 2; ++i) {
+        y[2 * i] = dot2_v(x2s[i], smask[i]);
+        y[2 * i + 1] = dot2_neghi(x2s[i], smask[i]);
+      }
     }
     // ---- FWHT stages 2..5 in registers
 #pragma unroll
@@ -310,6 +330,21 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
     if constexpr (LPB >= 8) {
       ORBQ_DPP_FMAC8("row_half_mirror", y, sgn3);
       ORBQ_DPP_FMAC8("row_half_mirror", y + 8, sgn3);
+    }
+    if constexpr (LPB >= 16) {
+      ORBQ_DPP_FMAC8("row_mirror", y, sgn4);
+      ORBQ_DPP_FMAC8("row_mirror", y + 8, sgn4);
+    }
+    if constexpr (LPB >= 32) {  // partner lane i xor 16 (within 32 lanes): ds_swizzle bit mode
+#pragma unroll
+      for (int e = 0; e < kE; ++e)
+        y[e] = __builtin_fmaf(sgn5, __builtin_bit_cast(float, __builtin_amdgcn_ds_swizzle(__builtin_bit_cast(int, y[e]), 0x401F)), y[e]);
+    }
+    if constexpr (LPB >= 64) {  // partner lane i xor 32
+      const int pa = (static_cast<int>(threadIdx.x & 63) ^ 32) << 2;
+#pragma unroll
+      for (int e = 0; e < kE; ++e)
+        y[e] = __builtin_fmaf(sgn6, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(pa, __builtin_bit_cast(int, y[e]))), y[e]);
     }
 
     // ---- token norm: the lane segments' partial sums, added in a fixed order
@@ -386,13 +421,13 @@ int device_cu_count();
 
 // Balanced persistent grid: every workgroup runs the same number of token groups, and all of
 // them are resident at once (as many workgroups per CU as the kernel's occupancy allows).
-template <int H, int BITS, QuantMode MODE>
+template <int H, int BITS, QuantMode MODE, bool PERM>
 hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
   static thread_local int cached_threads = -1, cached_occ = 1;
   static thread_local size_t cached_lds = 0;
   if (threads != cached_threads || lds != cached_lds) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_rpbh_quantize<H, BITS, MODE>, threads, lds) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_rpbh_quantize<H, BITS, MODE, PERM>, threads, lds) != hipSuccess ||
         occ < 1)
       occ = 1;
     cached_threads = threads;
@@ -402,22 +437,34 @@ hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, hipSt
   const int max_grid = device_cu_count() * cached_occ;
   const int iters = (a.ngroups + max_grid - 1) / max_grid;
   const int grid = (a.ngroups + iters - 1) / iters;
-  hipLaunchKernelGGL((k_rpbh_quantize<H, BITS, MODE>), dim3(grid), dim3(threads), lds, st, a);
+  hipLaunchKernelGGL((k_rpbh_quantize<H, BITS, MODE, PERM>), dim3(grid), dim3(threads), lds, st, a);
   return hipGetLastError();
+}
+
+template <int H, QuantMode MODE, bool PERM>
+hipError_t launch_perm(int bits, const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
+  if constexpr (MODE == QuantMode::kRotateOnly) return launch_typed<H, 4, MODE, PERM>(a, threads, lds, st);
+  switch (bits) {
+    case 2: return launch_typed<H, 2, MODE, PERM>(a, threads, lds, st);
+    case 4: return launch_typed<H, 4, MODE, PERM>(a, threads, lds, st);
+    default: return launch_typed<H, 6, MODE, PERM>(a, threads, lds, st);
+  }
 }
 
 template <int H, QuantMode MODE>
 hipError_t launch_bits(int bits, const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
-  switch (bits) {
-    case 2: return launch_typed<H, 2, MODE>(a, threads, lds, st);
-    case 4: return launch_typed<H, 4, MODE>(a, threads, lds, st);
-    default: return launch_typed<H, 6, MODE>(a, threads, lds, st);
-  }
+  return a.perm ? launch_perm<H, MODE, true>(bits, a, threads, lds, st) : launch_perm<H, MODE, false>(bits, a, threads, lds, st);
 }
 
 template <QuantMode MODE>
 hipError_t launch_mode(int block, int bits, const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
-  return block == 64 ? launch_bits<64, MODE>(bits, a, threads, lds, st) : launch_bits<128, MODE>(bits, a, threads, lds, st);
+  switch (block) {
+    case 64: return launch_bits<64, MODE>(bits, a, threads, lds, st);
+    case 128: return launch_bits<128, MODE>(bits, a, threads, lds, st);
+    case 256: return launch_bits<256, MODE>(bits, a, threads, lds, st);
+    case 512: return launch_bits<512, MODE>(bits, a, threads, lds, st);
+    default: return launch_bits<1024, MODE>(bits, a, threads, lds, st);
+  }
 }
 
 int device_cu_count() {

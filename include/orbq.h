@@ -44,7 +44,7 @@
  * signs) are read, never validated, by the kernels: a perm entry outside [0, d) is
  * clamped into range (garbage in, garbage out, no out-of-bounds access).
  *
- * Supported shapes: block in {64, 128}; d a multiple of block and at most 16384;
+ * Supported shapes: block a power of two in [64, 1024]; d a multiple of block and at most 16384;
  * activation bits and weight bits each in {2, 4, 6}.  n or m equal to 0 is a no-op.
  * Alignment: bf16 matrices and code buffers 16-byte aligned with row pitches that
  * are multiples of 16 bytes; norm arrays 4-byte (fp32) or 2-byte (bf16) aligned;
@@ -75,8 +75,12 @@ typedef enum { ORBQ_F32 = 0, ORBQ_BF16 = 1 } orbq_dtype;
 /* RPBH rotation for one dimension d (OrbitQuant summary, "Randomized Permuted
  * Block-Hadamard (RPBH) Rotation"; fixed once per dimension).
  *   d      dimension, multiple of block
- *   block  Hadamard block size h (64 or 128)
- *   perm   [device] int32[d], a permutation of 0..d-1: (P x)[j] = x[perm[j]]
+ *   block  Hadamard block size h, a power of two in [64, 1024] (the OrbitQuant summary's
+ *          "RPBH Rotation" takes the largest power of two dividing d by default; the layers
+ *          here use 128)
+ *   perm   [device] int32[d], a permutation of 0..d-1: (P x)[j] = x[perm[j]]; NULL means the
+ *          identity (the block randomized Hadamard transform without the permutation, the
+ *          "Block-RHT" row of the OrbitQuant summary's "Rotation Ablation (Table 3)")
  *   signs  [device] int8[d], each +1 or -1, applied to position j after the permutation
  * Both arrays 16-byte aligned (ORBQ_ERR_ALIGNMENT otherwise); they must stay valid until the
  * calls that use them have completed on their stream. */
@@ -103,8 +107,9 @@ typedef struct {
  * Returns ORBQ_OK or ORBQ_ERR_INVALID_ARG. */
 int orbq_codebook_lloyd_max(int32_t d, int32_t bits, float* centroids_out);
 
-/* Host only, O(d): checks that perm_host is a permutation of 0..d-1, signs_host holds only
- * +1/-1, block is supported and divides d.  Use it on the host copies before uploading. */
+/* Host only, O(d): checks that perm_host is a permutation of 0..d-1 (or NULL: identity),
+ * signs_host holds only +1/-1, block is supported and divides d.  Use it on the host copies
+ * before uploading. */
 int orbq_rpbh_validate(int32_t d, int32_t block, const int32_t* perm_host, const int8_t* signs_host);
 
 /* Host only: checks a codebook as every entry point does (see ORBQ_ERR_CODEBOOK). */

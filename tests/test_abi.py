@@ -63,6 +63,13 @@ def test_rpbh_validate():
     assert lib.orbq_rpbh_validate(d, 64, perm.ctypes.data, s2.ctypes.data) == -1
     assert lib.orbq_rpbh_validate(d, 32, perm.ctypes.data, signs.ctypes.data) == -2
     assert lib.orbq_rpbh_validate(192, 128, perm.ctypes.data, signs.ctypes.data) == -1
+    # Hadamard blocks: powers of two in [64, 1024]; perm NULL = identity
+    p2 = np.random.default_rng(1).permutation(2048).astype(np.int32)
+    s2 = np.ones(2048, np.int8)
+    for blk, want in ((64, 0), (256, 0), (1024, 0), (2048, -2), (96, -2), (32, -2)):
+        assert lib.orbq_rpbh_validate(2048, blk, p2.ctypes.data, s2.ctypes.data) == want, blk
+    assert lib.orbq_rpbh_validate(2048, 512, None, s2.ctypes.data) == 0
+    assert lib.orbq_rpbh_validate(2048, 512, p2.ctypes.data, None) == -1
 
 
 def _cb_struct(c, d, bits):

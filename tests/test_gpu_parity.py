@@ -84,6 +84,51 @@ def test_rotation_matches_dense_matrix(orbq, d, h, n):
     assert np.max(np.abs(s - nrm) / nrm) < 1e-6
 
 
+@pytest.mark.parametrize("d,h,ident", [(3072, 256, False), (3072, 512, False), (3072, 1024, False),
+                                        (1024, 1024, False), (3072, 128, True), (3072, 1024, True),
+                                        (512, 64, True)])
+def test_rotation_large_blocks_and_identity(orbq, d, h, ident):
+    """Hadamard blocks of 256..1024 (cross-lane stages by DPP row mirrors, swizzle and lane
+    exchange) and the identity permutation (perm = NULL), against the dense matrix."""
+    log(f"rotate d={d} h={h} identity={ident}")
+    perm, signs = workloads.rotation(d)
+    rot = orbq.Rotation.create(d, h, None if ident else perm, signs)
+    X = workloads.activations(9, d, seed=2000 + d + h, kind="heavy", outlier_frac=0.002)
+    xr, s = orbq.test_rotate(dev_bf16(X), rot)
+    xr, s = xr.cpu().numpy().astype(np.float64), s.cpu().numpy().astype(np.float64)
+    Xf = workloads.f64_from_bf16_bits(X)
+    Pi = oracle.rpbh_matrix(d, h, np.arange(d) if ident else perm, signs)
+    ref = oracle.rotate(Xf, Pi)
+    nrm = np.linalg.norm(Xf, axis=1)
+    err = np.abs(xr - ref) / nrm[:, None]
+    assert err.max() < 1e-5, err.max()
+    assert np.max(np.abs(s - nrm) / nrm) < 1e-6
+
+
+@pytest.mark.parametrize("h,ident,weights", [(1024, False, False), (128, True, False), (512, True, True)])
+def test_quantize_large_blocks_and_identity(orbq, h, ident, weights):
+    """Codes and norms with the larger blocks and without the permutation, against the oracle."""
+    d, n = 3072, 131
+    perm, signs = workloads.rotation(d)
+    rot = orbq.Rotation.create(d, h, None if ident else perm, signs)
+    cb, c = gpu_codebook(orbq, d, 4)
+    src = workloads.activations(n, d, seed=3000 + h, kind="heavy") if not weights else workloads.weights(n, d, 3001)
+    if weights:
+        codes, norms = orbq.fold_weights(dev_bf16(src), rot, cb)
+        norms = norms.float()
+    else:
+        codes, norms = orbq.rpbh_quantize(dev_bf16(src), rot, cb)
+    Pi = oracle.rpbh_matrix(d, h, np.arange(d) if ident else perm, signs)
+    k_ref, s_ref, T_ref = oracle.quantize_activations(workloads.f64_from_bf16_bits(src), Pi, c)
+    check_codes(oracle.unpack_codes(codes.cpu().numpy(), 4, d), k_ref, T_ref, c, f"h={h} identity={ident}")
+    got = norms.cpu().numpy().astype(np.float64)
+    if weights:
+        r_ref = oracle.bf16_rne(s_ref)
+        assert np.all(np.abs(got - r_ref) <= 2.0 ** (np.floor(np.log2(r_ref)) - 7))
+    else:
+        assert np.max(np.abs(got - s_ref) / s_ref) < 1e-6
+
+
 # ----------------------------------------------------------------- quantize / fold
 def _quant_case(orbq, name, rows=None, sample=None, weights=False):
     torch = torch_mod()
