@@ -89,6 +89,10 @@ def main() -> int:
                     help="seconds of untimed steps before the warmup steps (clock settle)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration) and exit")
+    ap.add_argument("--rotation-ablation", action="store_true",
+                    help="time rpbh_quantize under the rotation variants of the rotation ablation "
+                         "(RPBH, block RHT without permutation, RHT over 1024-wide blocks, dense Haar "
+                         "rotation as a bf16 GEMM) on the workload's activations; prints its own line")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample tokens (default: all)")
     ap.add_argument("--cpu-weights", type=int, default=None, help="oracle sample weight rows (default: all)")
     args = ap.parse_args()
@@ -128,6 +132,9 @@ def main() -> int:
     x_norms = torch.empty((L.n,), dtype=torch.float32, device=dev)
     Y = torch.empty((L.n, L.m), dtype=torch.bfloat16, device=dev)
     ws = torch.empty((orbq.linear_workspace_bytes(L.n, L.d, L.bits_a),), dtype=torch.uint8, device=dev)
+
+    if args.rotation_ablation:
+        return rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args)
 
     def quantize(Xin=X):
         orbq.rpbh_quantize(Xin, rot, cb_a, out_codes=x_codes, out_norms=x_norms)
@@ -257,6 +264,77 @@ def main() -> int:
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L, X_bits, W_bits, perm, signs, args.cpu_tokens, args.cpu_weights)
     print(json.dumps(line), flush=True)
+    return 0
+
+
+def _event_ms(fn, reps: int) -> float:
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    for _ in range(3):
+        fn()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        fn()
+    e1.record()
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args) -> int:
+    """The rotation ablation on one layer's activations: rpbh_quantize (rotate, normalise,
+    quantize, pack) under each rotation, back to back on the same resident input.
+      rpbh          block h = L.block with the random permutation (the method)
+      block_rht     block h = L.block, permutation = identity
+      rht_1024      h = 1024 (the widest power-of-two block dividing d, the whole vector when
+                    d = 1024), with and without the permutation
+      haar_dense    a dense d x d orthogonal rotation applied as a bf16 GEMM (torch / hipBLASLt);
+                    the rotation alone, without normalisation or quantization: a lower bound
+                    on a dense rotation's cost"""
+    import numpy as np
+    import torch
+
+    dev = X.device
+    x_codes = torch.empty((L.n, orbq.codes_row_bytes(L.d, L.bits_a)), dtype=torch.uint8, device=dev)
+    x_norms = torch.empty((L.n,), dtype=torch.float32, device=dev)
+    wide = 1
+    while wide < 1024 and L.d % (2 * wide) == 0:
+        wide *= 2
+    variants = [("rpbh", L.block, perm), ("block_rht", L.block, None),
+                (f"rht_{wide}_perm", wide, perm), (f"rht_{wide}", wide, None)]
+    reps = max(50, args.steps)
+    t_settle = time.perf_counter()
+    rot0 = orbq.Rotation.create(L.d, L.block, perm, signs)
+    while time.perf_counter() - t_settle < args.settle:
+        for _ in range(50):
+            orbq.rpbh_quantize(X, rot0, cb_a, out_codes=x_codes, out_norms=x_norms)
+        torch.cuda.synchronize()
+    res = {}
+    for vname, h, p in variants:
+        rot = orbq.Rotation.create(L.d, h, p, signs)
+        ms = _event_ms(lambda: orbq.rpbh_quantize(X, rot, cb_a, out_codes=x_codes, out_norms=x_norms), reps)
+        res[vname] = {"block": h, "permutation": p is not None, "us": round(ms * 1e3, 2)}
+    # dense orthogonal d x d rotation (QR of a Gaussian matrix; its exact distribution does not
+    # matter for the cost) applied to the bf16 activations
+    g = torch.Generator(device="cpu").manual_seed(5)
+    Q, _ = torch.linalg.qr(torch.randn((L.d, L.d), generator=g, dtype=torch.float32))
+    Phi_t = Q.t().contiguous().to(device=dev, dtype=torch.bfloat16)
+    Xr = torch.empty((L.n, L.d), dtype=torch.bfloat16, device=dev)
+    ms = _event_ms(lambda: torch.matmul(X, Phi_t, out=Xr), reps)
+    res["haar_dense_gemm"] = {"block": L.d, "permutation": False, "us": round(ms * 1e3, 2),
+                              "note": "rotation only (bf16 GEMM), no normalisation or quantization"}
+    base = res["rpbh"]["us"]
+    for v in res.values():
+        v["vs_rpbh"] = round(v["us"] / base, 3)
+    q_bytes = L.n * (2 * L.d + L.d * L.bits_a // 8 + 4)
+    for vname, _, _ in variants:
+        res[vname]["GBps"] = round(q_bytes / (res[vname]["us"] * 1e-6) / 1e9, 1)
+    print(json.dumps({"metric": "rotation ablation: rpbh_quantize time per rotation", "unit": "us",
+                      "higher_is_better": False, "n_gpus": 1, "reps": reps, "data": "synthetic",
+                      "config": {"workload": name, "tokens": L.n, "d": L.d, "bits_a": L.bits_a},
+                      "variants": res}), flush=True)
+    del Phi_t, Xr
     return 0
 
 
