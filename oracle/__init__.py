@@ -15,6 +15,9 @@ What it computes (OrbitQuant summary on picx.dev, "Methodology"):
                 ("Offline Weight Quantization", "Online Activation Quantization").
   linear.py     the dequantised product with the rotation cancelled, and the
                 packed code format written out from its documented definition.
+  activation.py GELU (erf and tanh forms) applied to the product, the activation
+                a fused MLP up-projection produces (Nunchaku / SVDQuant in
+                Diffusers, on fusing GELU with the MLP).
 
 Every function cites the passage it follows.  Each is pinned in
 tests/test_oracle_*.py against closed forms, printed values or brute force.
@@ -23,6 +26,7 @@ from .rpbh import hadamard, rpbh_matrix, rotate
 from .density import log_fd, fd, gaussian_limit_pdf, cell_mass, cell_moment, mean_abs_t
 from .lloyd_max import lloyd_max, thresholds_midpoint
 from .quantize import argmin_codes, rotate_normalize, quantize_activations, fold_weights, bf16_rne
+from .activation import ACTIVATIONS, activation, gelu_erf, gelu_tanh, lut_gemm_act
 from .linear import (decode_lut_bf16, lut_gemm, orbq_linear, unquantized_fold, to_sign_magnitude,
                      from_sign_magnitude, pack_codes, unpack_codes, codes_row_bytes)
 
@@ -31,5 +35,6 @@ __all__ = [
     "cell_moment", "mean_abs_t", "lloyd_max", "thresholds_midpoint", "argmin_codes",
     "rotate_normalize", "quantize_activations", "fold_weights", "bf16_rne", "decode_lut_bf16",
     "lut_gemm", "orbq_linear", "unquantized_fold", "to_sign_magnitude", "from_sign_magnitude",
-    "pack_codes", "unpack_codes", "codes_row_bytes",
+    "pack_codes", "unpack_codes", "codes_row_bytes", "ACTIVATIONS", "activation", "gelu_erf",
+    "gelu_tanh", "lut_gemm_act",
 ]
