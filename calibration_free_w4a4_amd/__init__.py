@@ -64,10 +64,15 @@ _SIGS = {
                                           _F, _P, _P, _P]),
     "orbq_lut_gemm": (ctypes.c_int, [_P, _P, ctypes.POINTER(_Codebook), _P, _P, ctypes.POINTER(_Codebook),
                                      _I64, _I64, _I64, _P, ctypes.c_int, _I64, _P]),
+    "orbq_lut_gemm_act": (ctypes.c_int, [_P, _P, ctypes.POINTER(_Codebook), _P, _P, ctypes.POINTER(_Codebook),
+                                         _I64, _I64, _I64, ctypes.c_int, _P, ctypes.c_int, _I64, _P]),
     "orbq_linear_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I32]),
     "orbq_linear": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), ctypes.POINTER(_Codebook), _F,
                                    _P, _P, ctypes.POINTER(_Codebook), _I64, _P, ctypes.c_size_t, _P,
                                    ctypes.c_int, _I64, _P]),
+    "orbq_linear_act": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), ctypes.POINTER(_Codebook), _F,
+                                       _P, _P, ctypes.POINTER(_Codebook), _I64, _P, ctypes.c_size_t, ctypes.c_int,
+                                       _P, ctypes.c_int, _I64, _P]),
     "orbq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "orbq_last_error": (ctypes.c_char_p, []),
     "orbq_test_rotate": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), _P, _P, _P]),
@@ -210,23 +215,41 @@ def rpbh_quantize(X, rot: Rotation, cb: Codebook, eps: float = 1e-8, out_codes=N
     return codes, norms
 
 
-def lut_gemm(x_codes, x_norms, cb_a: Codebook, w_codes, w_norms, cb_w: Codebook, d: int, out_dtype=None, out=None):
-    """Y [n, m] = diag(s) C_a[x_codes] C_w[w_codes]^T diag(r')."""
+ACTIVATIONS = {"none": 0, "gelu_tanh": 1, "gelu_erf": 2}   # orbq_activation
+
+
+def _act(act: str) -> int:
+    if act not in ACTIVATIONS:
+        raise ValueError(f"activation must be one of {sorted(ACTIVATIONS)}, not {act!r}")
+    return ACTIVATIONS[act]
+
+
+def lut_gemm(x_codes, x_norms, cb_a: Codebook, w_codes, w_norms, cb_w: Codebook, d: int, out_dtype=None, out=None,
+             act: str = "none"):
+    """Y [n, m] = act(diag(s) C_a[x_codes] C_w[w_codes]^T diag(r')); act "none" calls
+    orbq_lut_gemm, "gelu_tanh" / "gelu_erf" orbq_lut_gemm_act."""
     torch = _torch()
     out_dtype = out_dtype or torch.float32
     n, m = x_codes.shape[0], w_codes.shape[0]
     Y = out if out is not None else torch.empty((n, m), dtype=out_dtype, device=x_codes.device)
     a, w = cb_a.struct(), cb_w.struct()
-    _check(load().orbq_lut_gemm(x_codes.data_ptr(), x_norms.data_ptr(), ctypes.byref(a), w_codes.data_ptr(),
-                                w_norms.data_ptr(), ctypes.byref(w), n, m, d, Y.data_ptr(),
-                                BF16 if Y.dtype == torch.bfloat16 else F32, Y.stride(0),
-                                _stream(torch, x_codes.device)), "orbq_lut_gemm")
+    yt = BF16 if Y.dtype == torch.bfloat16 else F32
+    code = _act(act)
+    if code == 0:
+        _check(load().orbq_lut_gemm(x_codes.data_ptr(), x_norms.data_ptr(), ctypes.byref(a), w_codes.data_ptr(),
+                                    w_norms.data_ptr(), ctypes.byref(w), n, m, d, Y.data_ptr(), yt, Y.stride(0),
+                                    _stream(torch, x_codes.device)), "orbq_lut_gemm")
+    else:
+        _check(load().orbq_lut_gemm_act(x_codes.data_ptr(), x_norms.data_ptr(), ctypes.byref(a), w_codes.data_ptr(),
+                                        w_norms.data_ptr(), ctypes.byref(w), n, m, d, code, Y.data_ptr(), yt,
+                                        Y.stride(0), _stream(torch, x_codes.device)), "orbq_lut_gemm_act")
     return Y
 
 
 def linear(X, rot: Rotation, cb_a: Codebook, w_codes, w_norms, cb_w: Codebook, eps: float = 1e-8, out_dtype=None,
-           workspace=None, out=None):
-    """The online layer: Y [n, m] from bf16 tokens X [n, d] and folded weights."""
+           workspace=None, out=None, act: str = "none"):
+    """The online layer: Y [n, m] from bf16 tokens X [n, d] and folded weights (act as in
+    lut_gemm: "none" calls orbq_linear, a GELU form orbq_linear_act)."""
     torch = _torch()
     _dev_tensor(X, torch.bfloat16, "linear")
     out_dtype = out_dtype or torch.float32
@@ -237,11 +260,18 @@ def linear(X, rot: Rotation, cb_a: Codebook, w_codes, w_norms, cb_w: Codebook, e
         workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
     Y = out if out is not None else torch.empty((n, m), dtype=out_dtype, device=X.device)
     r, a, w = rot.struct(), cb_a.struct(), cb_w.struct()
-    _check(load().orbq_linear(X.data_ptr(), n, d, X.stride(0), ctypes.byref(r), ctypes.byref(a), eps,
-                              w_codes.data_ptr(), w_norms.data_ptr(), ctypes.byref(w), m, workspace.data_ptr(),
-                              workspace.numel() * workspace.element_size(), Y.data_ptr(),
-                              BF16 if Y.dtype == torch.bfloat16 else F32, Y.stride(0), _stream(torch, X.device)),
-           "orbq_linear")
+    yt = BF16 if Y.dtype == torch.bfloat16 else F32
+    ws_bytes = workspace.numel() * workspace.element_size()
+    code = _act(act)
+    if code == 0:
+        _check(load().orbq_linear(X.data_ptr(), n, d, X.stride(0), ctypes.byref(r), ctypes.byref(a), eps,
+                                  w_codes.data_ptr(), w_norms.data_ptr(), ctypes.byref(w), m, workspace.data_ptr(),
+                                  ws_bytes, Y.data_ptr(), yt, Y.stride(0), _stream(torch, X.device)), "orbq_linear")
+    else:
+        _check(load().orbq_linear_act(X.data_ptr(), n, d, X.stride(0), ctypes.byref(r), ctypes.byref(a), eps,
+                                      w_codes.data_ptr(), w_norms.data_ptr(), ctypes.byref(w), m, workspace.data_ptr(),
+                                      ws_bytes, code, Y.data_ptr(), yt, Y.stride(0), _stream(torch, X.device)),
+               "orbq_linear_act")
     return Y
 
 

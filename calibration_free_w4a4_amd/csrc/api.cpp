@@ -185,20 +185,34 @@ int gemm_checks(const uint8_t* x_codes, const float* x_norms, const orbq_codeboo
 
 int gemm_launch(const uint8_t* x_codes, const float* x_norms, const orbq_codebook* cb_a, const uint8_t* w_codes,
                 const void* w_norms, const orbq_codebook* cb_w, int64_t n, int64_t m, int64_t d, void* Y,
-                orbq_dtype y_type, int64_t ldy, void* stream, const char* what) {
+                orbq_dtype y_type, int64_t ldy, int act, void* stream, const char* what) {
   orbq::DecodeParams da, dw;
   orbq::build_decode_params(cb_a->centroids, cb_a->bits, &da);
   orbq::build_decode_params(cb_w->centroids, cb_w->bits, &dw);
   const int e = orbq::launch_lut_gemm(x_codes, x_norms, da, w_codes, static_cast<const uint16_t*>(w_norms), dw, n, m, d,
-                                      Y, y_type == ORBQ_BF16, ldy, static_cast<hipStream_t>(stream));
+                                      Y, y_type == ORBQ_BF16, ldy, act, static_cast<hipStream_t>(stream));
   return hip_status(e, what);
 }
+
+bool valid_act(int act) { return act == ORBQ_ACT_NONE || act == ORBQ_ACT_GELU_TANH || act == ORBQ_ACT_GELU_ERF; }
 
 size_t ws_codes_bytes(int64_t n, int64_t d, int32_t bits) {
   return (static_cast<size_t>(n) * static_cast<size_t>(d * bits / 8) + 255) & ~size_t(255);
 }
 
 }  // namespace
+
+ORBQ_API int orbq_lut_gemm_act(const uint8_t* x_codes, const float* x_norms, const orbq_codebook* cb_a,
+                               const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w, int64_t n,
+                               int64_t m, int64_t d, orbq_activation act, void* Y, orbq_dtype y_type, int64_t ldy,
+                               void* stream) {
+  const char* what = "orbq_lut_gemm_act";
+  if (!valid_act(act)) return fail(ORBQ_ERR_INVALID_ARG, "%s: unknown activation %d", what, static_cast<int>(act));
+  int s = gemm_checks(x_codes, x_norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, what, true);
+  if (s) return s;
+  if (n == 0 || m == 0) return ok();
+  return gemm_launch(x_codes, x_norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, act, stream, what);
+}
 
 ORBQ_API int orbq_lut_gemm(const uint8_t* x_codes, const float* x_norms, const orbq_codebook* cb_a,
                            const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w, int64_t n, int64_t m,
@@ -207,7 +221,8 @@ ORBQ_API int orbq_lut_gemm(const uint8_t* x_codes, const float* x_norms, const o
   int s = gemm_checks(x_codes, x_norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, what, true);
   if (s) return s;
   if (n == 0 || m == 0) return ok();
-  return gemm_launch(x_codes, x_norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, stream, what);
+  return gemm_launch(x_codes, x_norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, ORBQ_ACT_NONE, stream,
+                     what);
 }
 
 ORBQ_API size_t orbq_linear_workspace_bytes(int64_t n, int64_t d, int32_t bits_a) {
@@ -215,11 +230,12 @@ ORBQ_API size_t orbq_linear_workspace_bytes(int64_t n, int64_t d, int32_t bits_a
   return ws_codes_bytes(n, d, bits_a) + static_cast<size_t>(n) * sizeof(float);
 }
 
-ORBQ_API int orbq_linear(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
-                         const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
-                         const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes, void* Y,
-                         orbq_dtype y_type, int64_t ldy, void* stream) {
-  const char* what = "orbq_linear";
+namespace {
+
+int linear_impl(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot, const orbq_codebook* cb_a,
+                float eps, const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w, int64_t m,
+                void* workspace, size_t ws_bytes, int act, void* Y, orbq_dtype y_type, int64_t ldy, void* stream,
+                const char* what) {
   int s = gemm_checks(nullptr, nullptr, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, what, false);
   if (s) return s;
   if ((s = check_rot(rot, d, what))) return s;
@@ -233,7 +249,27 @@ ORBQ_API int orbq_linear(const void* X, int64_t n, int64_t d, int64_t ldx, const
   float* norms = reinterpret_cast<float*>(codes + ws_codes_bytes(n, d, cb_a->bits));
   s = quantize_rows(orbq::QuantMode::kActivations, X, n, d, ldx, rot, cb_a, eps, codes, norms, 4, stream, what);
   if (s) return s;
-  return gemm_launch(codes, norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, stream, what);
+  return gemm_launch(codes, norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, act, stream, what);
+}
+
+}  // namespace
+
+ORBQ_API int orbq_linear(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                         const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
+                         const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes, void* Y,
+                         orbq_dtype y_type, int64_t ldy, void* stream) {
+  return linear_impl(X, n, d, ldx, rot, cb_a, eps, w_codes, w_norms, cb_w, m, workspace, ws_bytes, ORBQ_ACT_NONE, Y,
+                     y_type, ldy, stream, "orbq_linear");
+}
+
+ORBQ_API int orbq_linear_act(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                             const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
+                             const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes,
+                             orbq_activation act, void* Y, orbq_dtype y_type, int64_t ldy, void* stream) {
+  const char* what = "orbq_linear_act";
+  if (!valid_act(act)) return fail(ORBQ_ERR_INVALID_ARG, "%s: unknown activation %d", what, static_cast<int>(act));
+  return linear_impl(X, n, d, ldx, rot, cb_a, eps, w_codes, w_norms, cb_w, m, workspace, ws_bytes, act, Y, y_type,
+                     ldy, stream, what);
 }
 
 ORBQ_API const char* orbq_status_string(int status) {

@@ -65,6 +65,6 @@ int launch_quantize_t(const float* t, int64_t count, const QuantParams& qp, uint
 int launch_lut_gemm(const uint8_t* x_codes, const float* x_norms, const DecodeParams& da,
                     const uint8_t* w_codes, const uint16_t* w_norms, const DecodeParams& dw,
                     int64_t n, int64_t m, int64_t d, void* Y, int y_bf16, int64_t ldy,
-                    hipStream_t stream);
+                    int act, hipStream_t stream);
 
 }  // namespace orbq

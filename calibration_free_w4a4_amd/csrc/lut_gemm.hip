@@ -22,7 +22,10 @@
 //     (8 rows x 8 chunks per wave) are free of bank conflicts.  One barrier per K tile.
 //   * schedule: inside a K tile every second MFMA is followed by half of one unit's decode (and
 //     its LDS store), so the decode of the next K tile runs in the shadow of the matrix cores.
-//   * epilogue: Y = acc * s_i * r'_j in fp32, stored as fp32 or bf16 (round to nearest even).
+//   * epilogue: Y = act(acc * s_i * r'_j) in fp32, stored as fp32 or bf16 (round to nearest
+//     even); act is the identity or GELU (tanh or erf form), the activation an MLP applies
+//     between its up- and down-projection (Nunchaku / SVDQuant in Diffusers, ai-papers.net,
+//     on fusing GELU with the MLP).
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -64,6 +67,7 @@ struct GemmArgs {
   int32_t xrow_bytes, wrow_bytes;
   int32_t nk;  // K tiles
   int32_t tiles_n, tiles_m;
+  int32_t act;  // kActNone, kActGeluTanh, kActGeluErf
   // 4-bit decode tables: low / high bytes of the 8 bf16 magnitudes, 4 per register
   uint32_t lt_lo_a, lt_hi_a, ht_lo_a, ht_hi_a;
   uint32_t lt_lo_w, lt_hi_w, ht_lo_w, ht_hi_w;
@@ -193,6 +197,45 @@ struct Unit<6> {
     return decode6(lo, hi, static_cast<const uint32_t*>(lut));
   }
   static __device__ __forceinline__ uint32_t col_bytes(uint32_t c) { return (6 * c) & ~3u; }
+};
+
+// ----------------------------------------------------------------------------- activations
+// GELU, tanh form: x/2 (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3), rewritten as the
+// logistic x / (1 + exp(-2u)) = x / (1 + 2^-z), z = x (k0 + k1 x^2), k0 = 2 sqrt(2/pi) log2(e),
+// k1 = 0.044715 k0.  Large negative x gives 2^-z = inf and 0; large positive x gives x.
+__device__ __forceinline__ float gelu_tanh(float x) {
+  const float z = x * __builtin_fmaf(0.10294324f, x * x, 2.3022082f);
+  return x * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-z));
+}
+
+// GELU, erf form: x Phi(x).  Phi(-|x|) = erfc(|x|/sqrt 2)/2 by Abramowitz & Stegun 7.1.26:
+// erfc(u) = (a1 q + a2 q^2 + a3 q^3 + a4 q^4 + a5 q^5) e^(-u^2), q = 1 / (1 + p u), with an
+// absolute error below 1.5e-7 for u >= 0 (the published constants p, a1..a5).  Evaluating
+// the small tail Phi(-|x|) directly avoids cancelling 1 - erf for negative x.
+__device__ __forceinline__ float gelu_erf(float x) {
+  const float ax = __builtin_fabsf(x);
+  const float q = __builtin_amdgcn_rcpf(__builtin_fmaf(0.23164189f, ax, 1.0f));  // p / sqrt 2
+  float poly = __builtin_fmaf(1.061405429f, q, -1.453152027f);
+  poly = __builtin_fmaf(poly, q, 1.421413741f);
+  poly = __builtin_fmaf(poly, q, -0.284496736f);
+  poly = __builtin_fmaf(poly, q, 0.254829592f);
+  const float e = __builtin_amdgcn_exp2f(-0.72134752f * ax * ax);  // e^(-x^2 / 2)
+  const float tail = 0.5f * poly * q * e;                           // Phi(-|x|)
+  return x * (x >= 0.0f ? 1.0f - tail : tail);
+}
+
+constexpr int kActNone = 0, kActGeluTanh = 1, kActGeluErf = 2;
+
+template <int ACT>
+__device__ __forceinline__ float activate(float v) {
+  if constexpr (ACT == kActGeluTanh) return gelu_tanh(v);
+  else if constexpr (ACT == kActGeluErf) return gelu_erf(v);
+  else return v;
+}
+
+template <int ACT>
+struct ActTag {
+  static constexpr int value = ACT;
 };
 
 // chunk swizzle of a staged row: chunk c of row r sits at c ^ ((r >> 1) & 7)
@@ -377,6 +420,9 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
   }
 
   // ---- epilogue: D[row][col] of a 32x32 tile: col = lane % 32, row = 8*(r/4) + 4*(lane/32) + r%4
+  // (the activation is a uniform kernel argument: one branch selects the epilogue's variant)
+  auto epilogue = [&](auto tag) {
+  constexpr int ACT = decltype(tag)::value;
   const bool full = row0 + BM <= a.n && col0 + BN <= a.m;
   constexpr int esz = OUT_BF16 ? 2 : 4;
   float rn[C::TJ];
@@ -404,7 +450,8 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
         const int so0 = static_cast<int>(rr0 * ldy * esz), so1 = static_cast<int>((rr0 + 1) * ldy * esz);
 #pragma unroll
         for (int j = 0; j < C::TJ; ++j) {
-          const float v0 = acc[i][j][r] * s0 * rn[j], v1 = acc[i][j][r + 1] * s1 * rn[j];
+          const float v0 = activate<ACT>(acc[i][j][r] * s0 * rn[j]);
+          const float v1 = activate<ACT>(acc[i][j][r + 1] * s1 * rn[j]);
           if constexpr (OUT_BF16) {
             typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
             const bf16x2_t p = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
@@ -438,14 +485,20 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
         __bf16* yrow = reinterpret_cast<__bf16*>(a.Y) + row * a.ldy;
 #pragma unroll
         for (int j = 0; j < C::TJ; ++j)
-          if (cols[j] < a.m) yrow[cols[j]] = static_cast<__bf16>(acc[i][j][r] * sr * rn[j]);
+          if (cols[j] < a.m) yrow[cols[j]] = static_cast<__bf16>(activate<ACT>(acc[i][j][r] * sr * rn[j]));
       } else {
         float* yrow = reinterpret_cast<float*>(a.Y) + row * a.ldy;
 #pragma unroll
         for (int j = 0; j < C::TJ; ++j)
-          if (cols[j] < a.m) yrow[cols[j]] = acc[i][j][r] * sr * rn[j];
+          if (cols[j] < a.m) yrow[cols[j]] = activate<ACT>(acc[i][j][r] * sr * rn[j]);
       }
     }
+  }
+  };
+  switch (a.act) {
+    case kActGeluTanh: epilogue(ActTag<kActGeluTanh>{}); break;
+    case kActGeluErf: epilogue(ActTag<kActGeluErf>{}); break;
+    default: epilogue(ActTag<kActNone>{}); break;
   }
 }
 
@@ -506,8 +559,9 @@ int device_cus() {
 
 int launch_lut_gemm(const uint8_t* x_codes, const float* x_norms, const DecodeParams& da, const uint8_t* w_codes,
                     const uint16_t* w_norms, const DecodeParams& dw, int64_t n, int64_t m, int64_t d, void* Y,
-                    int y_bf16, int64_t ldy, hipStream_t stream) {
+                    int y_bf16, int64_t ldy, int act, hipStream_t stream) {
   GemmArgs a{};
+  a.act = act;
   a.xs = x_norms;
   a.wn = w_norms;
   a.ldy = ldy;

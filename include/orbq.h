@@ -72,6 +72,15 @@ typedef enum {
 
 typedef enum { ORBQ_F32 = 0, ORBQ_BF16 = 1 } orbq_dtype;
 
+/* Activation applied to the product before it is stored (Nunchaku / SVDQuant in Diffusers,
+ * ai-papers.net, section on quantizing one's own model: GELU fused with the MLP).  The
+ * pages name GELU without a formula; both standard forms are offered:
+ *   ORBQ_ACT_GELU_TANH  x/2 (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3)))
+ *   ORBQ_ACT_GELU_ERF   x Phi(x), Phi the standard normal CDF (Abramowitz & Stegun 7.1.26,
+ *                       absolute error of Phi below 1e-7)
+ * evaluated in fp32 on the scaled fp32 product, before rounding to the output type. */
+typedef enum { ORBQ_ACT_NONE = 0, ORBQ_ACT_GELU_TANH = 1, ORBQ_ACT_GELU_ERF = 2 } orbq_activation;
+
 /* RPBH rotation for one dimension d (OrbitQuant summary, "Randomized Permuted
  * Block-Hadamard (RPBH) Rotation"; fixed once per dimension).
  *   d      dimension, multiple of block
@@ -150,6 +159,14 @@ int orbq_lut_gemm(const uint8_t* x_codes, const float* x_norms, const orbq_codeb
                   int64_t n, int64_t m, int64_t d, void* Y, orbq_dtype y_type, int64_t ldy,
                   void* stream);
 
+/* orbq_lut_gemm followed by an activation in its epilogue: Y[i][j] = act(s_i r'_j sum_k ...),
+ * the MLP up-projection with its GELU fused.  Arguments and errors as orbq_lut_gemm; an
+ * unknown `act` returns ORBQ_ERR_INVALID_ARG.  ORBQ_ACT_NONE gives orbq_lut_gemm's bits. */
+int orbq_lut_gemm_act(const uint8_t* x_codes, const float* x_norms, const orbq_codebook* cb_a,
+                      const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w,
+                      int64_t n, int64_t m, int64_t d, orbq_activation act, void* Y,
+                      orbq_dtype y_type, int64_t ldy, void* stream);
+
 /* Workspace bytes orbq_linear needs for n tokens of dimension d at bits_a: packed codes
  * (rounded up to 256 bytes) followed by n fp32 norms. */
 size_t orbq_linear_workspace_bytes(int64_t n, int64_t d, int32_t bits_a);
@@ -160,6 +177,12 @@ int orbq_linear(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpb
                 const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
                 const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes, void* Y,
                 orbq_dtype y_type, int64_t ldy, void* stream);
+
+/* orbq_linear with orbq_lut_gemm_act's activation in the product's epilogue. */
+int orbq_linear_act(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                    const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
+                    const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes,
+                    orbq_activation act, void* Y, orbq_dtype y_type, int64_t ldy, void* stream);
 
 /* Human-readable name of a status code, and the detail of the last error on this thread. */
 const char* orbq_status_string(int status);

@@ -272,6 +272,78 @@ def test_lut_gemm_from_oracle_codes(orbq):
     assert e < 1e-5
 
 
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu_erf"])
+@pytest.mark.parametrize("out_bf16", [False, True])
+@pytest.mark.parametrize("n,m", [(300, 520), (800, 400)])
+def test_lut_gemm_activation(orbq, act, out_bf16, n, m):
+    """GELU in the epilogue (orbq_lut_gemm_act) against the oracle's float64 GELU of the float64
+    product.  Norms are scaled so that the outputs span the whole GELU (|Y| up to ~50: the
+    curved middle and both tails); full and edge tiles."""
+    torch = torch_mod()
+    d, ba, bw, seed = 1536, 4, 4, 31
+    log(f"gemm+{act} n={n} m={m} d={d} bf16={out_bf16}")
+    ca_cb, ca = gpu_codebook(orbq, d, ba)
+    cw_cb, cw = gpu_codebook(orbq, d, bw)
+    xb = workloads.random_code_bytes(n, d * ba // 8, seed)
+    wb = workloads.random_code_bytes(m, d * bw // 8, seed + 1)
+    s = workloads.random_norms(n, seed + 2, 5.0, 20.0).astype(np.float32)
+    s[::17] *= 20.0  # some rows far into the tails
+    r_bits = workloads.bf16_bits_from_f64(workloads.random_norms(m, seed + 3, 1.0, 4.0))
+    Y = orbq.lut_gemm(torch.from_numpy(xb).cuda(), torch.from_numpy(s).cuda(), ca_cb,
+                      torch.from_numpy(wb).cuda(), dev_bf16(r_bits), cw_cb, d,
+                      out_dtype=torch.bfloat16 if out_bf16 else torch.float32, act=act)
+    torch.cuda.synchronize()
+    G = (Y.float() if out_bf16 else Y).cpu().numpy().astype(np.float64)
+    r = workloads.f64_from_bf16_bits(r_bits)
+    A = oracle.decode_lut_bf16(ca)[oracle.unpack_codes(xb, ba, d)]
+    B = oracle.decode_lut_bf16(cw)[oracle.unpack_codes(wb, bw, d)]
+    Yref = oracle.lut_gemm(oracle.unpack_codes(xb, ba, d), s.astype(np.float64), ca,
+                           oracle.unpack_codes(wb, bw, d), r, cw)
+    Gref = oracle.activation(Yref, act)
+    den = (np.abs(A) @ np.abs(B).T) * s.astype(np.float64)[:, None] * r[None, :]
+    e = float(np.max(np.abs(G - Gref) / den))
+    big = np.abs(Yref) > 0.5
+    fe = float(np.max(np.abs(G - Gref)[big] / np.maximum(np.abs(Gref[big]), 1e-3)))
+    log(f"  |Y| max {np.abs(Yref).max():.1f}; error / |dot| scale {e:.3g}; relative to |GELU(Y)| where |Y| > 0.5: {fe:.3g}")
+    assert np.abs(Yref).max() > 20 and (Yref < -3).any() and (Yref > 3).any()
+    # fp32: accumulation order and the fp32 GELU (< 1e-6 of |Y|); bf16 adds one rounding (2^-8)
+    assert e <= (2.0 ** -8 + 1e-5 if out_bf16 else 1e-5)
+    assert np.isfinite(G).all()
+
+
+def test_lut_gemm_act_none_and_linear_act(orbq):
+    """ACT_NONE through orbq_lut_gemm_act gives orbq_lut_gemm's bits; orbq_linear_act gives
+    rpbh_quantize then lut_gemm_act's bits."""
+    import ctypes
+    torch = torch_mod()
+    L = workloads.CONFIGS["tiny"]
+    X, W = workloads.layer_inputs(L)
+    rot = gpu_rotation(orbq, L.d, L.block)
+    cb, _ = gpu_codebook(orbq, L.d, 4)
+    dX, dW = dev_bf16(X), dev_bf16(W)
+    wc, wn = orbq.fold_weights(dW, rot, cb)
+    xc, xs = orbq.rpbh_quantize(dX, rot, cb)
+    Y0 = orbq.lut_gemm(xc, xs, cb, wc, wn, cb, L.d)
+    Y1 = torch.empty_like(Y0)
+    a = cb.struct()
+    st = orbq.load().orbq_lut_gemm_act(xc.data_ptr(), xs.data_ptr(), ctypes.byref(a), wc.data_ptr(), wn.data_ptr(),
+                                       ctypes.byref(a), L.n, L.m, L.d, 0, Y1.data_ptr(), 0, Y1.stride(0),
+                                       torch.cuda.current_stream().cuda_stream)
+    assert st == 0
+    st = orbq.load().orbq_lut_gemm_act(xc.data_ptr(), xs.data_ptr(), ctypes.byref(a), wc.data_ptr(), wn.data_ptr(),
+                                       ctypes.byref(a), L.n, L.m, L.d, 7, Y1.data_ptr(), 0, Y1.stride(0),
+                                       torch.cuda.current_stream().cuda_stream)
+    assert st == -1  # unknown activation
+    torch.cuda.synchronize()
+    assert torch.equal(Y0, Y1)
+    for act in ("gelu_tanh", "gelu_erf"):
+        for dt in (torch.float32, torch.bfloat16):
+            G1 = orbq.linear(dX, rot, cb, wc, wn, cb, act=act, out_dtype=dt)
+            G2 = orbq.lut_gemm(xc, xs, cb, wc, wn, cb, L.d, act=act, out_dtype=dt)
+            torch.cuda.synchronize()
+            assert torch.equal(G1, G2), (act, dt)
+
+
 # ----------------------------------------------------------------- the layer
 def test_linear_equals_quantize_then_gemm(orbq):
     torch = torch_mod()
