@@ -93,6 +93,10 @@ def main() -> int:
                     help="time rpbh_quantize under the rotation variants of the rotation ablation "
                          "(RPBH, block RHT without permutation, RHT over 1024-wide blocks, dense Haar "
                          "rotation as a bf16 GEMM) on the workload's activations; prints its own line")
+    ap.add_argument("--mlp", action="store_true",
+                    help="time the FLUX MLP pair (up-projection, GELU, down-projection; 9216 tokens, "
+                         "3072 -> 12288 -> 3072, W4A4) with GELU fused into the up-projection's "
+                         "epilogue against GELU as a separate pass; prints its own line")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample tokens (default: all)")
     ap.add_argument("--cpu-weights", type=int, default=None, help="oracle sample weight rows (default: all)")
     args = ap.parse_args()
@@ -117,6 +121,8 @@ def main() -> int:
     L = workloads.CONFIGS[name]
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
+    if args.mlp:
+        return mlp_pair(orbq, workloads, args)
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -335,6 +341,97 @@ def rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args) -> int:
                       "config": {"workload": name, "tokens": L.n, "d": L.d, "bits_a": L.bits_a},
                       "variants": res}), flush=True)
     del Phi_t, Xr
+    return 0
+
+
+def mlp_pair(orbq, workloads, args) -> int:
+    """The FLUX MLP pair on one batch: rpbh_quantize, lut_gemm (up) -> GELU -> rpbh_quantize,
+    lut_gemm (down), all bf16 between the layers.  Fused: GELU (tanh form) in the
+    up-projection's epilogue.  Unfused: the up-projection stores its raw product and torch's
+    GELU runs as a separate pass.  Each kernel is timed with HIP events over `reps` repetitions
+    of the whole pair, after the settle phase."""
+    import numpy as np
+    import torch
+    import torch.nn.functional as F
+
+    dev = torch.device("cuda", 0)
+    Lu, Ld = workloads.CONFIGS["flux_mlp_up"], workloads.CONFIGS["flux_mlp_down"]
+    n = Lu.n
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X_bits, Wu_bits = workloads.layer_inputs(Lu)
+    X, Wu, Wd = to_dev(X_bits), to_dev(Wu_bits), to_dev(workloads.weights(Ld.m, Ld.d, Ld.w_seed))
+    rot_u = orbq.Rotation.create(Lu.d, Lu.block, *workloads.rotation(Lu.d))
+    rot_d = orbq.Rotation.create(Ld.d, Ld.block, *workloads.rotation(Ld.d))
+    cb_u, cb_d = orbq.Codebook.lloyd_max(Lu.d, 4), orbq.Codebook.lloyd_max(Ld.d, 4)
+    wcu, wnu = orbq.fold_weights(Wu, rot_u, cb_u)
+    wcd, wnd = orbq.fold_weights(Wd, rot_d, cb_d)
+    xcu = torch.empty((n, orbq.codes_row_bytes(Lu.d, 4)), dtype=torch.uint8, device=dev)
+    xsu = torch.empty((n,), dtype=torch.float32, device=dev)
+    xcd = torch.empty((n, orbq.codes_row_bytes(Ld.d, 4)), dtype=torch.uint8, device=dev)
+    xsd = torch.empty((n,), dtype=torch.float32, device=dev)
+    H = torch.empty((n, Lu.m), dtype=torch.bfloat16, device=dev)
+    H2 = torch.empty_like(H)
+    Y = torch.empty((n, Ld.m), dtype=torch.bfloat16, device=dev)
+
+    def stages(fused: bool):
+        st = [lambda: orbq.rpbh_quantize(X, rot_u, cb_u, out_codes=xcu, out_norms=xsu)]
+        if fused:
+            st.append(lambda: orbq.lut_gemm(xcu, xsu, cb_u, wcu, wnu, cb_u, Lu.d, out=H, act="gelu_tanh"))
+        else:
+            st.append(lambda: orbq.lut_gemm(xcu, xsu, cb_u, wcu, wnu, cb_u, Lu.d, out=H2))
+            st.append(lambda: torch.ops.aten.gelu.out(H2, approximate="tanh", out=H))
+        st.append(lambda: orbq.rpbh_quantize(H, rot_d, cb_d, out_codes=xcd, out_norms=xsd))
+        st.append(lambda: orbq.lut_gemm(xcd, xsd, cb_d, wcd, wnd, cb_d, Ld.d, out=Y))
+        return st
+
+    names = {True: ["rpbh_quantize_up", "lut_gemm_up_gelu", "rpbh_quantize_down", "lut_gemm_down"],
+             False: ["rpbh_quantize_up", "lut_gemm_up", "gelu_pass", "rpbh_quantize_down", "lut_gemm_down"]}
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle:
+        for _ in range(5):
+            for f in stages(True):
+                f()
+        torch.cuda.synchronize()
+    reps = max(10, args.steps // 4)
+    out = {}
+    for fused in (True, False):
+        st = stages(fused)
+        for _ in range(3):
+            for f in st:
+                f()
+        ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(st) + 1)] for _ in range(reps)]
+        torch.cuda.synchronize()
+        w0 = time.perf_counter()
+        for k in range(reps):
+            for i, f in enumerate(st):
+                ev[k][i].record()
+                f()
+            ev[k][len(st)].record()
+        torch.cuda.synchronize()
+        wall = (time.perf_counter() - w0) * 1e3 / reps
+        per = {nm: round(statistics.mean(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(reps)) * 1e3, 2)
+               for i, nm in enumerate(names[fused])}
+        out["fused" if fused else "unfused"] = {"us_per_kernel": per, "ms_per_pair": round(wall, 4)}
+    flops = 2.0 * n * Lu.d * Lu.m + 2.0 * n * Ld.d * Ld.m
+    torch.cuda.synchronize()
+    # the fused up-projection equals torch's GELU of the unfused one (to bf16 rounding)
+    Hf = torch.empty_like(H)
+    orbq.lut_gemm(xcu, xsu, cb_u, wcu, wnu, cb_u, Lu.d, out=Hf, act="gelu_tanh")
+    ref = F.gelu(H2.float(), approximate="tanh")
+    agree = float(((Hf.float() - ref).abs() / ref.abs().clamp_min(1e-2)).max())
+    for k in out:
+        out[k]["TFLOPs"] = round(flops / (out[k]["ms_per_pair"] * 1e-3) / 1e12, 1)
+    print(json.dumps({"metric": "FLUX MLP pair (up, GELU, down) time per batch, GELU fused vs separate",
+                      "unit": "ms", "higher_is_better": False, "n_gpus": 1, "reps": reps, "data": "synthetic",
+                      "dtype": "bf16",
+                      "config": {"workload": "flux_mlp_pair", "tokens": n, "d": Lu.d, "hidden": Lu.m,
+                                 "bits_w": 4, "bits_a": 4, "block": Lu.block, "gelu": "tanh"},
+                      "fused": out["fused"], "unfused": out["unfused"],
+                      "saving_ms": round(out["unfused"]["ms_per_pair"] - out["fused"]["ms_per_pair"], 4),
+                      "fused_vs_torch_gelu_max_rel_diff": round(agree, 5)}), flush=True)
     return 0
 
 
