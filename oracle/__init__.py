@@ -6,7 +6,9 @@ never calls it, and it never calls the HIP library: the two share no code.
 
 What it computes (OrbitQuant summary on picx.dev, "Methodology"):
   rpbh.py       the RPBH rotation as an explicit dense d x d matrix
-                ("Randomized Permuted Block-Hadamard (RPBH) Rotation").
+                ("Randomized Permuted Block-Hadamard (RPBH) Rotation"), its
+                composition over several passes and the O(d) flatness statistics
+                ("Quantizing With Randomized Hadamard Transforms", gist.science).
   density.py    the sphere-coordinate marginal f_d and its cell integrals
                 ("Theoretical Basis", item 1).
   lloyd_max.py  the Lloyd-Max codebook for f_d by plain Lloyd iteration
@@ -22,7 +24,7 @@ What it computes (OrbitQuant summary on picx.dev, "Methodology"):
 Every function cites the passage it follows.  Each is pinned in
 tests/test_oracle_*.py against closed forms, printed values or brute force.
 """
-from .rpbh import hadamard, rpbh_matrix, rotate
+from .rpbh import flatness, hadamard, rotate, rpbh_composed, rpbh_matrix
 from .density import log_fd, fd, gaussian_limit_pdf, cell_mass, cell_moment, mean_abs_t
 from .lloyd_max import lloyd_max, thresholds_midpoint
 from .quantize import argmin_codes, rotate_normalize, quantize_activations, fold_weights, bf16_rne
@@ -31,7 +33,7 @@ from .linear import (decode_lut_bf16, lut_gemm, orbq_linear, unquantized_fold, t
                      from_sign_magnitude, pack_codes, unpack_codes, codes_row_bytes)
 
 __all__ = [
-    "hadamard", "rpbh_matrix", "rotate", "log_fd", "fd", "gaussian_limit_pdf", "cell_mass",
+    "hadamard", "rpbh_matrix", "rotate", "rpbh_composed", "flatness", "log_fd", "fd", "gaussian_limit_pdf", "cell_mass",
     "cell_moment", "mean_abs_t", "lloyd_max", "thresholds_midpoint", "argmin_codes",
     "rotate_normalize", "quantize_activations", "fold_weights", "bf16_rne", "decode_lut_bf16",
     "lut_gemm", "orbq_linear", "unquantized_fold", "to_sign_magnitude", "from_sign_magnitude",

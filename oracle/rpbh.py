@@ -52,3 +52,40 @@ def rotate(X: np.ndarray, Pi: np.ndarray) -> np.ndarray:
     """x' = Pi x for every row x of X, i.e. X Pi^T ("Online Activation
     Quantization", step 1: applied as x Pi^T for token batches)."""
     return np.asarray(X, dtype=np.float64) @ Pi.T
+
+
+def rpbh_composed(d: int, h: int, perm, signs: np.ndarray, passes: int) -> np.ndarray:
+    """Pi = Pi_{passes-1} ... Pi_1 Pi_0 (float64 [d, d]): `passes` RPBH rotations applied one
+    after the other, pass p with permutation perm[p d:(p+1) d] (None: the identity) and signs
+    signs[p d:(p+1) d].
+
+    "Quantizing With Randomized Hadamard Transforms" (gist.science), "Method": the composition
+    R_k of k randomized Hadamard transforms, each a Hadamard matrix times its own Rademacher
+    diagonal; here each factor is a whole RPBH pass, whose permutation mixes across blocks.
+    """
+    signs = np.asarray(signs)
+    Pi = np.eye(d)
+    for p in range(passes):
+        pp = np.arange(d) if perm is None else np.asarray(perm)[p * d:(p + 1) * d]
+        Pi = rpbh_matrix(d, h, pp, signs[p * d:(p + 1) * d]) @ Pi
+    return Pi
+
+
+def flatness(X: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-row (rho3, rhoinf) = (sqrt(d) ||x||_3^3 / ||x||_2^3, sqrt(d) ||x||_inf / ||x||_2),
+    both 0 for a zero row.
+
+    "Quantizing With Randomized Hadamard Transforms", "Method" (adaptive check): an O(d) look
+    at the input's l3 norm (scalar quantization) or l_inf norm (vector quantization) tells
+    whether it is already flat enough for fewer randomized Hadamard transforms.  Scaled so
+    that a constant vector gives 1 and a one-hot vector sqrt(d).
+    """
+    X = np.asarray(X, dtype=np.float64)
+    d = X.shape[1]
+    l2 = np.sqrt(np.sum(X * X, axis=1))
+    l3c = np.sum(np.abs(X) ** 3, axis=1)
+    linf = np.max(np.abs(X), axis=1)
+    safe = np.where(l2 > 0, l2, 1.0)
+    rho3 = np.where(l2 > 0, np.sqrt(d) * l3c / safe ** 3, 0.0)
+    rhoinf = np.where(l2 > 0, np.sqrt(d) * linf / safe, 0.0)
+    return rho3, rhoinf

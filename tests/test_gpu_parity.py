@@ -1,6 +1,6 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU oracle on seeded inputs.
 
-Tolerances (north star of this layer):
+Tolerances (the layer's stated parity bar):
   * codes bit-exact except coordinates within 1e-5 (t units) of a decision boundary,
     counted, at most 1e-5 of all coordinates;
   * product from identical codes within 2e-3 max error relative to s_i r'_j sum|C_a C_w|

@@ -54,7 +54,7 @@ def test_rpbh_factor_order_and_conventions(d, h):
 
 
 def test_rotation_cancels_in_unquantized_product():
-    """(X Pi^T)(W Pi^T)^T = X W^T (spec bound 1e-5 relative; float64 gives ~1e-15)."""
+    """(X Pi^T)(W Pi^T)^T = X W^T: the rotation cancels (bound 1e-5 relative; float64 gives ~1e-15)."""
     d, h = 384, 128
     perm, signs = workloads.rotation(d)
     Pi = oracle.rpbh_matrix(d, h, perm, signs)
@@ -69,3 +69,53 @@ def test_rotation_cancels_in_unquantized_product():
 def test_rpbh_rejects_non_permutation():
     with pytest.raises(ValueError):
         oracle.rpbh_matrix(128, 64, np.zeros(128, np.int64), np.ones(128))
+
+
+# ---------------------------------------------------------------- composed passes, flatness
+def test_composed_single_pass_is_rpbh():
+    perm, signs = workloads.rotation(256)
+    assert np.array_equal(oracle.rpbh_composed(256, 64, perm, signs, 1), oracle.rpbh_matrix(256, 64, perm, signs))
+
+
+def test_composed_order_by_hadamard_involution():
+    """(H/sqrt h)^2 = I: a second pass with the identity permutation and all signs +1 undoes the
+    first pass's block transform, leaving the signed permutation D_0 P_0 (Pi[j, perm[j]] =
+    signs[j]).  Composing in the other order would leave dense blocks."""
+    d, h = 512, 128
+    perm, signs = workloads.rotation(d)
+    P2 = np.concatenate([perm, np.arange(d, dtype=np.int32)])
+    S2 = np.concatenate([signs, np.ones(d, np.int8)])
+    Pi = oracle.rpbh_composed(d, h, P2, S2, 2)
+    want = np.zeros((d, d))
+    want[np.arange(d), perm] = signs
+    assert np.max(np.abs(Pi - want)) < 1e-12
+
+
+def test_composed_is_orthogonal_and_mixes_a_spike():
+    d, h = 1024, 64
+    p0, s0 = workloads.rotation(d)
+    p1, s1 = workloads.rotation(d, seed=d + 7)
+    Pi2 = oracle.rpbh_composed(d, h, np.concatenate([p0, p1]), np.concatenate([s0, s1]), 2)
+    assert np.max(np.abs(Pi2 @ Pi2.T - np.eye(d))) < 1e-12
+    # a one-hot input: one pass spreads it over exactly one block (h entries of 1/sqrt(h), so
+    # rho3 = sqrt(d / h) exactly); the second pass spreads it over many blocks
+    e = np.zeros((1, d)); e[0, 5] = 1.0
+    one = oracle.rotate(e, oracle.rpbh_matrix(d, h, p0, s0))
+    r1, _ = oracle.flatness(one)
+    assert abs(r1[0] - np.sqrt(d / h)) < 1e-12 and np.count_nonzero(np.abs(one) > 1e-12) == h
+    r2, _ = oracle.flatness(oracle.rotate(e, Pi2))
+    assert r2[0] < 0.5 * r1[0]
+
+
+def test_flatness_closed_forms():
+    d = 4096
+    X = np.zeros((4, d))
+    X[0] = 3.0                       # constant: rho3 = rhoinf = 1
+    X[1, 17] = -2.5                  # one-hot: sqrt(d) for both
+    X[3] = np.random.default_rng(0).standard_normal(d)  # Gaussian: rho3 -> E|g|^3 = 2 sqrt(2/pi)
+    r3, ri = oracle.flatness(X)
+    assert abs(r3[0] - 1) < 1e-12 and abs(ri[0] - 1) < 1e-12
+    assert abs(r3[1] - 64) < 1e-12 and abs(ri[1] - 64) < 1e-12
+    assert r3[2] == 0 and ri[2] == 0  # zero row
+    assert abs(r3[3] - 2 * np.sqrt(2 / np.pi)) < 0.05
+    assert 2.5 < ri[3] < 5.5          # max of d Gaussians ~ sqrt(2 ln d) = 4.08
