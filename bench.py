@@ -295,11 +295,14 @@ def rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args) -> int:
       block_rht     block h = L.block, permutation = identity
       rht_1024      h = 1024 (the widest power-of-two block dividing d, the whole vector when
                     d = 1024), with and without the permutation
+      rpbh_2pass, rpbh_3pass  two / three composed RPBH passes, each with its own permutation and
+                    signs (composed randomized Hadamard transforms)
       haar_dense    a dense d x d orthogonal rotation applied as a bf16 GEMM (torch / hipBLASLt);
                     the rotation alone, without normalisation or quantization: a lower bound
                     on a dense rotation's cost"""
-    import numpy as np
     import torch
+
+    import workloads
 
     dev = X.device
     x_codes = torch.empty((L.n, orbq.codes_row_bytes(L.d, L.bits_a)), dtype=torch.uint8, device=dev)
@@ -307,8 +310,10 @@ def rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args) -> int:
     wide = 1
     while wide < 1024 and L.d % (2 * wide) == 0:
         wide *= 2
-    variants = [("rpbh", L.block, perm), ("block_rht", L.block, None),
-                (f"rht_{wide}_perm", wide, perm), (f"rht_{wide}", wide, None)]
+    p3, s3 = workloads.rotation_passes(L.d, 3)
+    variants = [("rpbh", L.block, perm, signs, 1), ("block_rht", L.block, None, signs, 1),
+                (f"rht_{wide}_perm", wide, perm, signs, 1), (f"rht_{wide}", wide, None, signs, 1),
+                ("rpbh_2pass", L.block, p3[:2 * L.d], s3[:2 * L.d], 2), ("rpbh_3pass", L.block, p3, s3, 3)]
     reps = max(50, args.steps)
     t_settle = time.perf_counter()
     rot0 = orbq.Rotation.create(L.d, L.block, perm, signs)
@@ -317,10 +322,10 @@ def rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args) -> int:
             orbq.rpbh_quantize(X, rot0, cb_a, out_codes=x_codes, out_norms=x_norms)
         torch.cuda.synchronize()
     res = {}
-    for vname, h, p in variants:
-        rot = orbq.Rotation.create(L.d, h, p, signs)
+    for vname, h, p, sg, k in variants:
+        rot = orbq.Rotation.create(L.d, h, p, sg, passes=k)
         ms = _event_ms(lambda: orbq.rpbh_quantize(X, rot, cb_a, out_codes=x_codes, out_norms=x_norms), reps)
-        res[vname] = {"block": h, "permutation": p is not None, "us": round(ms * 1e3, 2)}
+        res[vname] = {"block": h, "permutation": p is not None, "passes": k, "us": round(ms * 1e3, 2)}
     # dense orthogonal d x d rotation (QR of a Gaussian matrix; its exact distribution does not
     # matter for the cost) applied to the bf16 activations
     g = torch.Generator(device="cpu").manual_seed(5)
@@ -334,7 +339,7 @@ def rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args) -> int:
     for v in res.values():
         v["vs_rpbh"] = round(v["us"] / base, 3)
     q_bytes = L.n * (2 * L.d + L.d * L.bits_a // 8 + 4)
-    for vname, _, _ in variants:
+    for vname, *_ in variants:
         res[vname]["GBps"] = round(q_bytes / (res[vname]["us"] * 1e-6) / 1e9, 1)
     print(json.dumps({"metric": "rotation ablation: rpbh_quantize time per rotation", "unit": "us",
                       "higher_is_better": False, "n_gpus": 1, "reps": reps, "data": "synthetic",

@@ -42,7 +42,7 @@ class OrbqError(RuntimeError):
 
 class _Rpbh(ctypes.Structure):
     _fields_ = [("d", ctypes.c_int32), ("block", ctypes.c_int32), ("perm", ctypes.c_void_p),
-                ("signs", ctypes.c_void_p)]
+                ("signs", ctypes.c_void_p), ("passes", ctypes.c_int32)]
 
 
 class _Codebook(ctypes.Structure):
@@ -73,6 +73,8 @@ _SIGS = {
     "orbq_linear_act": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), ctypes.POINTER(_Codebook), _F,
                                        _P, _P, ctypes.POINTER(_Codebook), _I64, _P, ctypes.c_size_t, ctypes.c_int,
                                        _P, ctypes.c_int, _I64, _P]),
+    "orbq_rpbh_flatness": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "orbq_rht_passes": (ctypes.c_int32, [ctypes.c_float, ctypes.c_float, _I32, _I32]),
     "orbq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "orbq_last_error": (ctypes.c_char_p, []),
     "orbq_test_rotate": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), _P, _P, _P]),
@@ -122,27 +124,32 @@ def _dev_tensor(t, dtype, name):
 # ---------------------------------------------------------------- descriptors
 @dataclass
 class Rotation:
-    """RPBH rotation for dimension d: device perm (int32[d], or None for the identity) and
-    signs (int8[d])."""
+    """RPBH rotation for dimension d: device perm (int32[passes * d], or None for the identity)
+    and signs (int8[passes * d]); passes > 1 composes that many RPBH passes."""
     d: int
     block: int
     perm: "object"
     signs: "object"
+    passes: int = 1
 
     @classmethod
-    def create(cls, d: int, block: int, perm, signs: np.ndarray, device=None) -> "Rotation":
+    def create(cls, d: int, block: int, perm, signs: np.ndarray, device=None, passes: int = 1) -> "Rotation":
         signs = np.ascontiguousarray(signs, dtype=np.int8)
         if perm is not None:
             perm = np.ascontiguousarray(perm, dtype=np.int32)
-        _check(load().orbq_rpbh_validate(d, block, None if perm is None else perm.ctypes.data, signs.ctypes.data),
-               "orbq_rpbh_validate")
+        if signs.size != passes * d or (perm is not None and perm.size != passes * d):
+            raise OrbqError(-1, "Rotation", f"{passes} passes need perm and signs of {passes * d} entries")
+        for p in range(passes):  # each pass is one RPBH rotation
+            _check(load().orbq_rpbh_validate(d, block, None if perm is None else perm[p * d:].ctypes.data,
+                                             signs[p * d:].ctypes.data), "orbq_rpbh_validate")
         torch = _torch()
         dev = device or torch.device("cuda", torch.cuda.current_device())
         dperm = None if perm is None else torch.from_numpy(perm).to(dev)
-        return cls(d, block, dperm, torch.from_numpy(signs).to(dev))
+        return cls(d, block, dperm, torch.from_numpy(signs).to(dev), passes)
 
     def struct(self) -> _Rpbh:
-        return _Rpbh(self.d, self.block, 0 if self.perm is None else self.perm.data_ptr(), self.signs.data_ptr())
+        return _Rpbh(self.d, self.block, 0 if self.perm is None else self.perm.data_ptr(), self.signs.data_ptr(),
+                     self.passes)
 
 
 @dataclass
@@ -273,6 +280,27 @@ def linear(X, rot: Rotation, cb_a: Codebook, w_codes, w_norms, cb_w: Codebook, e
                                       ws_bytes, code, Y.data_ptr(), yt, Y.stride(0), _stream(torch, X.device)),
                "orbq_linear_act")
     return Y
+
+
+def flatness(X):
+    """(rho3, rhoinf) fp32 [n] of bf16 rows X [n, d]: sqrt(d) ||x||_3^3 / ||x||_2^3 and
+    sqrt(d) ||x||_inf / ||x||_2 (orbq_rpbh_flatness)."""
+    torch = _torch()
+    _dev_tensor(X, torch.bfloat16, "flatness")
+    n, d = X.shape
+    rho3 = torch.empty((n,), dtype=torch.float32, device=X.device)
+    rhoinf = torch.empty((n,), dtype=torch.float32, device=X.device)
+    _check(load().orbq_rpbh_flatness(X.data_ptr(), n, d, X.stride(0), rho3.data_ptr(), rhoinf.data_ptr(),
+                                     _stream(torch, X.device)), "orbq_rpbh_flatness")
+    return rho3, rhoinf
+
+
+def rht_passes(rho3: float, rhoinf: float, d: int, vector_quantization: bool = False) -> int:
+    """Composed passes the adaptive check asks for (orbq_rht_passes)."""
+    r = load().orbq_rht_passes(float(rho3), float(rhoinf), d, int(vector_quantization))
+    if r < 0:
+        _check(r, "orbq_rht_passes")
+    return r
 
 
 def test_rotate(X, rot: Rotation):

@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liborbq.so")
 ARCH = os.environ.get("ORBQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "codebook.cpp", "rpbh_quantize.hip", "lut_gemm.hip"]
+SOURCES = ["api.cpp", "codebook.cpp", "rpbh_quantize.hip", "lut_gemm.hip", "flatness.hip"]
 
 
 def hipcc() -> str:

@@ -58,6 +58,8 @@ int check_rot(const orbq_rpbh* rot, int64_t d, const char* what) {
   if (rot->block < 64 || rot->block > 1024 || (rot->block & (rot->block - 1)))
     return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not a power of two in [64, 1024]", what, rot->block);
   if (d % rot->block) return fail(ORBQ_ERR_INVALID_ARG, "%s: d=%lld not a multiple of block %d", what, (long long)d, rot->block);
+  if (rot->passes < 0 || rot->passes > 3)
+    return fail(ORBQ_ERR_UNSUPPORTED, "%s: %d composed passes (0..3 supported)", what, rot->passes);
   if ((rot->perm && !aligned(rot->perm, 16)) || !aligned(rot->signs, 16))
     return fail(ORBQ_ERR_ALIGNMENT, "%s: rotation arrays must be 16-byte aligned", what);
   return ORBQ_OK;
@@ -98,7 +100,7 @@ int quantize_rows(orbq::QuantMode mode, const void* X, int64_t n, int64_t d, int
   if (!aligned(norms, norm_align)) return fail(ORBQ_ERR_ALIGNMENT, "%s: norms misaligned", what);
   orbq::QuantParams qp;
   if ((s = quant_params(cb, &qp, what))) return s;
-  orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs};
+  orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs, rot->passes < 1 ? 1 : rot->passes};
   const int e = orbq::launch_rpbh_quantize(mode, static_cast<const uint16_t*>(X), n, ld, ra, &qp, eps, codes, norms,
                                            nullptr, static_cast<hipStream_t>(stream));
   return hip_status(e, what);
@@ -272,6 +274,32 @@ ORBQ_API int orbq_linear_act(const void* X, int64_t n, int64_t d, int64_t ldx, c
                      ldy, stream, what);
 }
 
+ORBQ_API int orbq_rpbh_flatness(const void* X, int64_t n, int64_t d, int64_t ldx, float* rho3, float* rhoinf,
+                                void* stream) {
+  const char* what = "orbq_rpbh_flatness";
+  int s;
+  if ((s = check_dim(d, what))) return s;
+  if (d % 8) return fail(ORBQ_ERR_UNSUPPORTED, "%s: d=%lld not a multiple of 8", what, (long long)d);
+  if (n < 0 || ldx < d) return fail(ORBQ_ERR_INVALID_ARG, "%s: bad n or ldx", what);
+  if (n == 0) return ok();
+  if (!X || !rho3 || !rhoinf) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL buffer", what);
+  if (!aligned(X, 16) || (ldx * 2) % 16 || !aligned(rho3, 4) || !aligned(rhoinf, 4))
+    return fail(ORBQ_ERR_ALIGNMENT, "%s: input must be 16-byte aligned with a 16-byte pitch", what);
+  const int e = orbq::launch_flatness(static_cast<const uint16_t*>(X), n, static_cast<int32_t>(d), ldx, rho3, rhoinf,
+                                      static_cast<hipStream_t>(stream));
+  return hip_status(e, what);
+}
+
+ORBQ_API int32_t orbq_rht_passes(float rho3, float rhoinf, int32_t d, int32_t vector_quantization) {
+  if (!(rho3 >= 0.0f) || !(rhoinf >= 0.0f) || d < 2) return ORBQ_ERR_INVALID_ARG;
+  // a Gaussian row has rho3 -> E|g|^3 = 2 sqrt(2/pi) and rhoinf ~ sqrt(2 ln(2d))
+  const double g3 = 2.0 * std::sqrt(2.0 / 3.14159265358979323846);
+  const double ginf = std::sqrt(2.0 * std::log(2.0 * d));
+  if (!vector_quantization) return rho3 <= 2.0 * g3 ? 1 : 2;
+  if (rhoinf <= ginf) return 1;
+  return rhoinf <= 2.0 * ginf ? 2 : 3;
+}
+
 ORBQ_API const char* orbq_status_string(int status) {
   switch (status) {
     case ORBQ_OK: return "ORBQ_OK";
@@ -298,7 +326,7 @@ ORBQ_API int orbq_test_rotate(const void* X, int64_t n, int64_t d, int64_t ldx, 
   if (!X || !x_rot || !x_norms) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL buffer", what);
   if (!aligned(X, 16) || (ldx * 2) % 16 || !aligned(x_rot, 16))
     return fail(ORBQ_ERR_ALIGNMENT, "%s: misaligned buffer", what);
-  orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs};
+  orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs, rot->passes < 1 ? 1 : rot->passes};
   const int e = orbq::launch_rpbh_quantize(orbq::QuantMode::kRotateOnly, static_cast<const uint16_t*>(X), n, ldx, ra,
                                            nullptr, 0.0f, nullptr, x_norms, x_rot, static_cast<hipStream_t>(stream));
   return hip_status(e, what);

@@ -51,6 +51,7 @@ struct RotArgs {
   int32_t d, block;
   const int32_t* perm;
   const int8_t* signs;
+  int32_t passes;  // composed passes (1..3); perm and signs hold passes * d entries
 };
 
 enum class QuantMode { kActivations, kWeights, kRotateOnly };
@@ -58,6 +59,9 @@ enum class QuantMode { kActivations, kWeights, kRotateOnly };
 int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t ldx, const RotArgs& rot,
                          const QuantParams* qp, float eps, uint8_t* codes, void* norms, float* x_rot,
                          hipStream_t stream);
+
+int launch_flatness(const uint16_t* X, int64_t n, int32_t d, int64_t ldx, float* rho3, float* rhoinf,
+                    hipStream_t stream);
 
 int launch_quantize_t(const float* t, int64_t count, const QuantParams& qp, uint8_t* codes,
                       hipStream_t stream);

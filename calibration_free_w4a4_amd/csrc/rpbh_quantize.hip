@@ -59,6 +59,9 @@ struct QuantKernelArgs {
   float inv_scale; // 2^k / sqrt(h) (quantize) or 1 / sqrt(h) (rotate only)
   uint32_t codes_bytes, norms_bytes, rot_bytes;  // buffer extents (< 2^31) for bounds-dropped stores
   uint32_t x_bytes;                              // extent of X in this launch (< 2^31)
+  int32_t passes;                                // composed RPBH passes (1..3)
+  uint32_t xf_off;                               // LDS byte offset of the fp32 rows (passes > 1)
+  float rsqrt_h;                                 // 1 / sqrt(h), the scale of each earlier pass
   QuantParams qp;
 };
 
@@ -171,7 +174,11 @@ __device__ __forceinline__ float segment_sum(float x, int seg) {
   return x;
 }
 
-template <int H, int BITS, QuantMode MODE, bool PERM>
+// MULTI: the rotation is the composition Pi_P ... Pi_1 of a.passes RPBH passes, pass p with its
+// own permutation and signs at perm + p d, signs + p d (RHT page, composed randomized Hadamard
+// transforms).  Between passes the fp32 rotated row goes through LDS for the next gather (or
+// stays in registers when the permutations are the identity).
+template <int H, int BITS, QuantMode MODE, bool PERM, bool MULTI>
 __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int d = a.d;
@@ -307,7 +314,8 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
         y[2 * i + 1] = dot2_neghi(x2s[i], smask[i]);
       }
     }
-    // ---- FWHT stages 2..5 in registers
+    // ---- FWHT stages 2..4 in registers, then the cross-lane stages
+    auto fwht_tail = [&](float (&y)[kE]) {
 #pragma unroll
     for (int st = 2; st < kE; st <<= 1) {
 #pragma unroll
@@ -345,6 +353,52 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
 #pragma unroll
       for (int e = 0; e < kE; ++e)
         y[e] = __builtin_fmaf(sgn6, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(pa, __builtin_bit_cast(int, y[e]))), y[e]);
+    }
+    };
+    fwht_tail(y);
+
+    if constexpr (MULTI) {
+      // passes 2.. : y holds pass p's output at positions j0 + e (unscaled, sign lane_sign)
+      float* xrow = reinterpret_cast<float*>(smem + a.xf_off) + slot * d;
+      for (int p = 1; p < a.passes; ++p) {
+        const float sc = lane_sign * a.rsqrt_h;
+#pragma unroll
+        for (int e = 0; e < kE; ++e) y[e] *= sc;
+        float g[kE];
+        if constexpr (PERM) {
+          if (p > 1) __syncthreads();  // the previous pass's gathers from xrow are done
+          if (active) {  // idle lanes alias slot 0's first positions
+#pragma unroll
+            for (int c = 0; c < kE / 4; ++c)
+              *reinterpret_cast<float4*>(xrow + j0 + 4 * c) = make_float4(y[4 * c], y[4 * c + 1], y[4 * c + 2], y[4 * c + 3]);
+          }
+          __syncthreads();
+          const int4* pp = reinterpret_cast<const int4*>(a.perm + static_cast<int64_t>(p) * d + j0);
+#pragma unroll
+          for (int c = 0; c < kE / 4; ++c) {
+            const int4 p4 = pp[c];
+            g[4 * c] = xrow[min(max(p4.x, 0), d - 1)];
+            g[4 * c + 1] = xrow[min(max(p4.y, 0), d - 1)];
+            g[4 * c + 2] = xrow[min(max(p4.z, 0), d - 1)];
+            g[4 * c + 3] = xrow[min(max(p4.w, 0), d - 1)];
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < kE; ++e) g[e] = y[e];
+        }
+        // signs of pass p (sign bit of each int8 into the fp32 sign), then FWHT stage 1
+        const uint4 sv = *reinterpret_cast<const uint4*>(a.signs + static_cast<int64_t>(p) * d + j0);
+        const uint32_t sw4[4] = {sv.x, sv.y, sv.z, sv.w};
+#pragma unroll
+        for (int e = 0; e < kE; ++e)
+          g[e] = __builtin_bit_cast(float, __builtin_bit_cast(uint32_t, g[e]) ^ (((sw4[e >> 2] >> (8 * (e & 3) + 7)) & 1u) << 31));
+#pragma unroll
+        for (int i = 0; i < kE / 2; ++i) {
+          y[2 * i] = g[2 * i] + g[2 * i + 1];
+          y[2 * i + 1] = g[2 * i] - g[2 * i + 1];
+        }
+        fwht_tail(y);
+      }
     }
 
     // ---- token norm: the lane segments' partial sums, added in a fixed order
@@ -421,13 +475,13 @@ int device_cu_count();
 
 // Balanced persistent grid: every workgroup runs the same number of token groups, and all of
 // them are resident at once (as many workgroups per CU as the kernel's occupancy allows).
-template <int H, int BITS, QuantMode MODE, bool PERM>
+template <int H, int BITS, QuantMode MODE, bool PERM, bool MULTI>
 hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
   static thread_local int cached_threads = -1, cached_occ = 1;
   static thread_local size_t cached_lds = 0;
   if (threads != cached_threads || lds != cached_lds) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_rpbh_quantize<H, BITS, MODE, PERM>, threads, lds) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_rpbh_quantize<H, BITS, MODE, PERM, MULTI>, threads, lds) != hipSuccess ||
         occ < 1)
       occ = 1;
     cached_threads = threads;
@@ -437,23 +491,27 @@ hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, hipSt
   const int max_grid = device_cu_count() * cached_occ;
   const int iters = (a.ngroups + max_grid - 1) / max_grid;
   const int grid = (a.ngroups + iters - 1) / iters;
-  hipLaunchKernelGGL((k_rpbh_quantize<H, BITS, MODE, PERM>), dim3(grid), dim3(threads), lds, st, a);
+  hipLaunchKernelGGL((k_rpbh_quantize<H, BITS, MODE, PERM, MULTI>), dim3(grid), dim3(threads), lds, st, a);
   return hipGetLastError();
 }
 
-template <int H, QuantMode MODE, bool PERM>
+template <int H, QuantMode MODE, bool PERM, bool MULTI>
 hipError_t launch_perm(int bits, const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
-  if constexpr (MODE == QuantMode::kRotateOnly) return launch_typed<H, 4, MODE, PERM>(a, threads, lds, st);
+  if constexpr (MODE == QuantMode::kRotateOnly) return launch_typed<H, 4, MODE, PERM, MULTI>(a, threads, lds, st);
   switch (bits) {
-    case 2: return launch_typed<H, 2, MODE, PERM>(a, threads, lds, st);
-    case 4: return launch_typed<H, 4, MODE, PERM>(a, threads, lds, st);
-    default: return launch_typed<H, 6, MODE, PERM>(a, threads, lds, st);
+    case 2: return launch_typed<H, 2, MODE, PERM, MULTI>(a, threads, lds, st);
+    case 4: return launch_typed<H, 4, MODE, PERM, MULTI>(a, threads, lds, st);
+    default: return launch_typed<H, 6, MODE, PERM, MULTI>(a, threads, lds, st);
   }
 }
 
 template <int H, QuantMode MODE>
 hipError_t launch_bits(int bits, const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
-  return a.perm ? launch_perm<H, MODE, true>(bits, a, threads, lds, st) : launch_perm<H, MODE, false>(bits, a, threads, lds, st);
+  if (a.passes > 1)
+    return a.perm ? launch_perm<H, MODE, true, true>(bits, a, threads, lds, st)
+                  : launch_perm<H, MODE, false, true>(bits, a, threads, lds, st);
+  return a.perm ? launch_perm<H, MODE, true, false>(bits, a, threads, lds, st)
+                : launch_perm<H, MODE, false, false>(bits, a, threads, lds, st);
 }
 
 template <QuantMode MODE>
@@ -491,6 +549,7 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
   a.ldx = ldx;
   a.perm = rot.perm;
   a.signs = rot.signs;
+  a.passes = rot.passes < 1 ? 1 : rot.passes;
   a.codes = codes;
   a.norms = norms;
   a.x_rot = x_rot;
@@ -523,8 +582,14 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
   const float rsqrt_h = 1.0f / __builtin_sqrtf(static_cast<float>(rot.block));
   a.inv_scale = (mode == QuantMode::kRotateOnly) ? rsqrt_h : static_cast<float>(static_cast<double>(a.qp.scale) /
                                                                                  std::sqrt(static_cast<double>(rot.block)));
-  const size_t lds = ((static_cast<size_t>(a.tg) * rot.d * 2 + 15) & ~size_t(15)) +
-                     sizeof(float2) * 2 * a.qp.J + sizeof(float) * a.tg * a.nseg;
+  size_t lds = ((static_cast<size_t>(a.tg) * rot.d * 2 + 15) & ~size_t(15)) +
+               sizeof(float2) * 2 * a.qp.J + sizeof(float) * a.tg * a.nseg;
+  a.rsqrt_h = rsqrt_h;
+  if (a.passes > 1 && a.perm) {  // fp32 rows for the gathers of the later passes
+    lds = (lds + 15) & ~size_t(15);
+    a.xf_off = static_cast<uint32_t>(lds);
+    lds += sizeof(float) * a.tg * rot.d;
+  }
   // rows per launch: every buffer extent (input rows, codes, norms, rotated rows) stays below 2^31 bytes
   const int64_t bytes_per_row = std::max<int64_t>(std::max<int64_t>(rot.d * 4, rot.d), ldx * 2);
   const int64_t chunk_rows = std::max<int64_t>(a.tg, ((int64_t(1) << 31) - 4096) / bytes_per_row / a.tg * a.tg);

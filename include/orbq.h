@@ -92,12 +92,21 @@ typedef enum { ORBQ_ACT_NONE = 0, ORBQ_ACT_GELU_TANH = 1, ORBQ_ACT_GELU_ERF = 2 
  *          "Block-RHT" row of the OrbitQuant summary's "Rotation Ablation (Table 3)")
  *   signs  [device] int8[d], each +1 or -1, applied to position j after the permutation
  * Both arrays 16-byte aligned (ORBQ_ERR_ALIGNMENT otherwise); they must stay valid until the
- * calls that use them have completed on their stream. */
+ * calls that use them have completed on their stream.
+ *   passes 0 or 1: one RPBH pass.  2 or 3: the composition Pi = Pi_passes ... Pi_1 of that
+ *          many RPBH passes ("Quantizing With Randomized Hadamard Transforms", gist.science:
+ *          composing two randomized Hadamard transforms gives Gaussian scalar marginals for
+ *          any input, three bound the coordinates' conditional covariance), pass p (from 0)
+ *          with its own permutation perm + p*d and signs signs + p*d, so both arrays then
+ *          hold passes*d entries (perm NULL: every pass without permutation).  Weights folded
+ *          with a composed rotation pair only with activations quantized with the same one.
+ *          Other values: ORBQ_ERR_UNSUPPORTED. */
 typedef struct {
   int32_t d;
   int32_t block;
   const int32_t* perm;
   const int8_t* signs;
+  int32_t passes;
 } orbq_rpbh;
 
 /* Lloyd-Max codebook for (d, bits) ("Theoretical Basis" item 2).
@@ -183,6 +192,26 @@ int orbq_linear_act(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq
                     const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
                     const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes,
                     orbq_activation act, void* Y, orbq_dtype y_type, int64_t ldy, void* stream);
+
+/* The adaptive check ("Quantizing With Randomized Hadamard Transforms", gist.science,
+ * "Method": an O(d) look at the input's l3 norm, for scalar quantization, or its l_inf
+ * norm, for vector quantization, decides whether 1, 2 or 3 composed transforms are needed).
+ *   X       [device] bf16[n][ldx], 16-byte aligned, 16-byte pitch; d a multiple of 8
+ *   rho3    [device] float[n], sqrt(d) ||x||_3^3 / ||x||_2^3 (1: constant row, sqrt(d): one-hot)
+ *   rhoinf  [device] float[n], sqrt(d) ||x||_inf / ||x||_2 (same scale)
+ * A zero row gives 0 for both.  fp32 sums (relative error ~1e-6).  One HBM pass over X. */
+int orbq_rpbh_flatness(const void* X, int64_t n, int64_t d, int64_t ldx, float* rho3,
+                       float* rhoinf, void* stream);
+
+/* [host] Pass count for a row (or the largest statistics of a batch or a weight matrix) with
+ * the given flatness.  The pages give the rule's inputs but no thresholds; this reading
+ * compares against a Gaussian row (rho3 -> 2 sqrt(2/pi), rhoinf ~ sqrt(2 ln 2d)):
+ *   scalar quantization (vector_quantization = 0): 1 if rho3 <= 2 * 2 sqrt(2/pi), else 2;
+ *   vector quantization: 1 if rhoinf <= sqrt(2 ln 2d), 2 if <= 2 sqrt(2 ln 2d), else 3.
+ * In the layer the rotation is fixed per dimension and shared with the folded weights, so the
+ * count is a per-layer choice, not a per-token one.  Negative statistics or d < 2:
+ * ORBQ_ERR_INVALID_ARG. */
+int32_t orbq_rht_passes(float rho3, float rhoinf, int32_t d, int32_t vector_quantization);
 
 /* Human-readable name of a status code, and the detail of the last error on this thread. */
 const char* orbq_status_string(int status);

@@ -153,6 +153,44 @@ def test_argument_errors_return_before_launch(cb):
               P, 0, 8, None) == -4
     assert ln(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, ctypes.byref(c4), 8, P + 16, need,
               P, 0, 8, None) == -3
+    # composed passes: 0..3 accepted, others unsupported (checked before any launch)
+    rot4 = orbq._Rpbh(d, 64, 0x1000, 0x2000, 4)
+    assert q(P, 8, d, d, ctypes.byref(rot4), ctypes.byref(c4), 1e-8, P, P, None) == -2
+    rotm = orbq._Rpbh(d, 64, 0x1000, 0x2000, -1)
+    assert q(P, 8, d, d, ctypes.byref(rotm), ctypes.byref(c4), 1e-8, P, P, None) == -2
+    assert q(None, 0, d, d, ctypes.byref(orbq._Rpbh(d, 64, 0x1000, 0x2000, 3)), ctypes.byref(c4), 1e-8,
+             None, None, None) == 0
+    # activation entry points
+    ga = lib.orbq_lut_gemm_act
+    assert ga(P, P, ctypes.byref(c4), P, P, ctypes.byref(c4), 8, 8, d, 3, P, 0, 8, None) == -1   # activation
+    assert ga(P, P, ctypes.byref(c4), P, P, ctypes.byref(c4), 8, 8, d, 1, P, 0, 4, None) == -1   # ldy < m
+    assert ga(P, P, ctypes.byref(c4), P, P, ctypes.byref(c4), 0, 8, d, 2, P, 0, 8, None) == 0    # empty
+    la = lib.orbq_linear_act
+    assert la(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, ctypes.byref(c4), 8, P, need,
+              -1, P, 0, 8, None) == -1
+    # flatness
+    fl = lib.orbq_rpbh_flatness
+    assert fl(P, 8, d, d - 8, P, P, None) == -1          # ldx < d
+    assert fl(P, 8, 252, 256, P, P, None) == -2          # d not a multiple of 8
+    assert fl(P + 2, 8, d, d, P, P, None) == -3          # misaligned rows
+    assert fl(None, 0, d, d, None, None, None) == 0      # empty
     # quantize_t
     assert lib.orbq_test_quantize_t(P, -1, ctypes.byref(c4), P, None) == -1
     assert lib.orbq_test_quantize_t(P, 0, ctypes.byref(c4), P, None) == 0
+
+
+def test_rht_passes_rule():
+    """Host rule of the adaptive check: against a Gaussian row's statistics."""
+    import math
+    lib = orbq.load()
+    d = 3072
+    g3 = 2 * math.sqrt(2 / math.pi)
+    ginf = math.sqrt(2 * math.log(2 * d))
+    assert lib.orbq_rht_passes(1.0, 1.0, d, 0) == 1               # constant row
+    assert lib.orbq_rht_passes(g3, 4.0, d, 0) == 1                # Gaussian-like
+    assert lib.orbq_rht_passes(math.sqrt(d), math.sqrt(d), d, 0) == 2   # one-hot
+    assert lib.orbq_rht_passes(math.sqrt(d), math.sqrt(d), d, 1) == 3
+    assert lib.orbq_rht_passes(1.0, ginf * 0.99, d, 1) == 1
+    assert lib.orbq_rht_passes(1.0, ginf * 1.5, d, 1) == 2
+    assert lib.orbq_rht_passes(-1.0, 1.0, d, 0) == -1
+    assert lib.orbq_rht_passes(float("nan"), 1.0, d, 0) == -1

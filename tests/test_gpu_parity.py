@@ -129,6 +129,82 @@ def test_quantize_large_blocks_and_identity(orbq, h, ident, weights):
         assert np.max(np.abs(got - s_ref) / s_ref) < 1e-6
 
 
+@pytest.mark.parametrize("d,h,passes,ident", [(3072, 128, 2, False), (3072, 128, 3, False), (256, 64, 3, False),
+                                               (1024, 1024, 2, True), (3072, 256, 2, True), (1536, 512, 2, False)])
+def test_rotation_composed_passes(orbq, d, h, passes, ident):
+    """Composed RPBH passes (each with its own permutation and signs; identity permutations
+    keep the later passes in registers) against the oracle's dense product of the passes."""
+    log(f"rotate d={d} h={h} passes={passes} identity={ident}")
+    perm, signs = workloads.rotation_passes(d, passes)
+    rot = orbq.Rotation.create(d, h, None if ident else perm, signs, passes=passes)
+    X = workloads.activations(11, d, seed=4000 + d + passes, kind="heavy", outlier_frac=0.002)
+    xr, s = orbq.test_rotate(dev_bf16(X), rot)
+    xr, s = xr.cpu().numpy().astype(np.float64), s.cpu().numpy().astype(np.float64)
+    Xf = workloads.f64_from_bf16_bits(X)
+    ref = oracle.rotate(Xf, oracle.rpbh_composed(d, h, None if ident else perm, signs, passes))
+    nrm = np.linalg.norm(Xf, axis=1)
+    err = np.abs(xr - ref) / nrm[:, None]
+    assert err.max() < 1e-5, err.max()
+    assert np.max(np.abs(s - nrm) / nrm) < 1e-6
+
+
+@pytest.mark.parametrize("passes,weights,kind", [(2, False, "heavy"), (2, True, "weights"), (3, False, "spikes")])
+def test_quantize_composed_passes(orbq, passes, weights, kind):
+    """Codes and norms through composed passes against the oracle, including one-hot tokens
+    (the inputs a single pass handles worst)."""
+    d, h, n = 3072, 128, 77
+    perm, signs = workloads.rotation_passes(d, passes)
+    rot = orbq.Rotation.create(d, h, perm, signs, passes=passes)
+    cb, c = gpu_codebook(orbq, d, 4)
+    if kind == "spikes":
+        # a spike per token plus a little noise (exact one-hot rows rotate onto a lattice of
+        # t values, which may sit within the boundary tolerance of a threshold)
+        f = workloads.f64_from_bf16_bits(workloads.activations(n, d, seed=6)) * 1e-2
+        f[np.arange(n), np.random.default_rng(5).integers(0, d, n)] += 3.0
+        src = workloads.bf16_bits_from_f64(f)
+    elif kind == "weights":
+        src = workloads.weights(n, d, 3101)
+    else:
+        src = workloads.activations(n, d, seed=3100, kind="heavy")
+    if weights:
+        codes, norms = orbq.fold_weights(dev_bf16(src), rot, cb)
+        norms = norms.float()
+    else:
+        codes, norms = orbq.rpbh_quantize(dev_bf16(src), rot, cb)
+    Pi = oracle.rpbh_composed(d, h, perm, signs, passes)
+    k_ref, s_ref, T_ref = oracle.quantize_activations(workloads.f64_from_bf16_bits(src), Pi, c)
+    check_codes(oracle.unpack_codes(codes.cpu().numpy(), 4, d), k_ref, T_ref, c, f"passes={passes} {kind}")
+    got = norms.cpu().numpy().astype(np.float64)
+    if weights:
+        r_ref = oracle.bf16_rne(s_ref)
+        assert np.all(np.abs(got - r_ref) <= 2.0 ** (np.floor(np.log2(r_ref)) - 7))
+    else:
+        assert np.max(np.abs(got - s_ref) / s_ref) < 1e-6
+
+
+def test_flatness_statistics(orbq):
+    """orbq_rpbh_flatness against the oracle on heavy-tailed tokens plus a zero, a constant and
+    a one-hot row (ragged row count); orbq_rht_passes on their statistics."""
+    torch = torch_mod()
+    d, n = 3072, 1003
+    X = workloads.activations(n, d, seed=77, kind="heavy")
+    X[5] = 0
+    X[6] = workloads.bf16_bits_from_f64(np.full(d, 0.75))
+    X[7] = 0; X[7, 123] = workloads.bf16_bits_from_f64(np.array([-2.0]))[0]
+    r3, ri = orbq.flatness(dev_bf16(X))
+    torch.cuda.synchronize()
+    r3, ri = r3.cpu().numpy().astype(np.float64), ri.cpu().numpy().astype(np.float64)
+    e3, ei = oracle.flatness(workloads.f64_from_bf16_bits(X))
+    assert np.max(np.abs(r3 - e3) / np.maximum(e3, 1e-30)) < 2e-5
+    assert np.max(np.abs(ri - ei) / np.maximum(ei, 1e-30)) < 2e-5
+    assert r3[5] == 0 and ri[5] == 0
+    assert abs(r3[6] - 1) < 1e-5 and abs(ri[6] - 1) < 1e-5
+    assert abs(r3[7] - math.sqrt(d)) < 1e-3 and abs(ri[7] - math.sqrt(d)) < 1e-3
+    assert orbq.rht_passes(r3[7], ri[7], d) == 2 and orbq.rht_passes(r3[7], ri[7], d, True) == 3
+    assert orbq.rht_passes(r3[6], ri[6], d) == 1 and orbq.rht_passes(r3[6], ri[6], d, True) == 1
+    assert orbq.flatness(dev_bf16(X[:0]))[0].numel() == 0
+
+
 # ----------------------------------------------------------------- quantize / fold
 def _quant_case(orbq, name, rows=None, sample=None, weights=False):
     torch = torch_mod()

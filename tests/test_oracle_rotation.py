@@ -119,3 +119,27 @@ def test_flatness_closed_forms():
     assert r3[2] == 0 and ri[2] == 0  # zero row
     assert abs(r3[3] - 2 * np.sqrt(2 / np.pi)) < 0.05
     assert 2.5 < ri[3] < 5.5          # max of d Gaussians ~ sqrt(2 ln d) = 4.08
+
+
+def test_two_passes_recover_gaussian_distortion_on_spikes():
+    """The composed-transform claim ("Quantizing With Randomized Hadamard Transforms": two
+    transforms give Gaussian scalar marginals for any input) in the layer's own terms: one-hot
+    tokens quantized after one RPBH pass (h nonzero coordinates, the rest exactly 0) lose ~20x
+    more than Gaussian tokens; after two passes they lose what Gaussian tokens lose."""
+    from tests.conftest import oracle_codebook
+    d, h = 3072, 128
+    c = oracle_codebook(d, 4)
+    P, S = workloads.rotation_passes(d, 2)
+    rng = np.random.default_rng(0)
+    spikes = np.zeros((12, d)); spikes[np.arange(12), rng.integers(0, d, 12)] = 1.0
+    gauss = rng.standard_normal((12, d))
+
+    def nmse(X, k):
+        Pi = oracle.rpbh_composed(d, h, P, S, k)
+        codes, s, _ = oracle.quantize_activations(X, Pi, c)
+        err = c[codes] * s[:, None] - oracle.rotate(X, Pi)
+        return float(np.mean(np.sum(err ** 2, axis=1) / np.sum(X ** 2, axis=1)))
+
+    g1, s1, s2 = nmse(gauss, 1), nmse(spikes, 1), nmse(spikes, 2)
+    assert s1 > 10 * g1
+    assert abs(s2 - g1) < 0.25 * g1

@@ -59,6 +59,13 @@ def rotation(d: int, seed: int | None = None) -> tuple[np.ndarray, np.ndarray]:
     return perm, signs
 
 
+def rotation_passes(d: int, passes: int) -> tuple[np.ndarray, np.ndarray]:
+    """`passes` independent (perm, signs) draws back to back (int32[passes d], int8[passes d]):
+    pass 0 is rotation(d), pass p > 0 uses seed d + 1000003 p."""
+    draws = [rotation(d, None if p == 0 else d + 1000003 * p) for p in range(passes)]
+    return (np.concatenate([x[0] for x in draws]), np.concatenate([x[1] for x in draws]))
+
+
 # ----------------------------------------------------------- activation inputs
 def activations(n: int, d: int, seed: int, kind: str = "heavy",
                 outlier_frac: float = 0.001, outlier_gain: float = 30.0,
