@@ -97,6 +97,10 @@ def main() -> int:
                     help="time the FLUX MLP pair (up-projection, GELU, down-projection; 9216 tokens, "
                          "3072 -> 12288 -> 3072, W4A4) with GELU fused into the up-projection's "
                          "epilogue against GELU as a separate pass; prints its own line")
+    ap.add_argument("--a16", action="store_true",
+                    help="time the weight-only product (bf16 activations, 4-bit weight codes) on the FLUX "
+                         "AdaLN modulation shape (2 x 3072 -> 18432) against torch's bf16 GEMM of the dense "
+                         "weights; prints its own line")
     ap.add_argument("--cpu-tokens", type=int, default=None, help="oracle sample tokens (default: all)")
     ap.add_argument("--cpu-weights", type=int, default=None, help="oracle sample weight rows (default: all)")
     args = ap.parse_args()
@@ -123,6 +127,8 @@ def main() -> int:
     torch.cuda.set_device(dev)
     if args.mlp:
         return mlp_pair(orbq, workloads, args)
+    if args.a16:
+        return a16_modulation(orbq, workloads, args)
 
     def to_dev(bits):
         return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -437,6 +443,52 @@ def mlp_pair(orbq, workloads, args) -> int:
                       "fused": out["fused"], "unfused": out["unfused"],
                       "saving_ms": round(out["unfused"]["ms_per_pair"] - out["fused"]["ms_per_pair"], 4),
                       "fused_vs_torch_gelu_max_rel_diff": round(agree, 5)}), flush=True)
+    return 0
+
+
+def a16_modulation(orbq, workloads, args) -> int:
+    """Weight-only product on the FLUX AdaLN modulation shape: 2 tokens (a CFG pair of
+    conditioning vectors) x 3072 -> 18432 (six modulation vectors), 4-bit weight codes, bf16
+    activations and output.  One call = rotate the tokens, stream the codes, add the K splits.
+    Bytes per call: the codes, r', X in and Y out; `achieved` is those bytes over the mean call
+    time (HIP events around 200 back-to-back calls)."""
+    import numpy as np
+    import torch
+
+    n, d, m, bw = 2, 3072, 18432, 4
+    dev = torch.device("cuda", 0)
+
+    def to_dev(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).to(dev)
+
+    X = to_dev(workloads.activations(n, d, seed=602, kind="heavy"))
+    W = to_dev(workloads.weights(m, d, 601))
+    rot = orbq.Rotation.create(d, 128, *workloads.rotation(d))
+    cb = orbq.Codebook.lloyd_max(d, bw)
+    wc, wn = orbq.fold_weights(W, rot, cb)
+    ws = torch.empty((orbq.linear_a16_workspace_bytes(n, d, m),), dtype=torch.uint8, device=dev)
+    Y = torch.empty((n, m), dtype=torch.bfloat16, device=dev)
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < args.settle:
+        for _ in range(200):
+            orbq.linear_a16(X, rot, wc, wn, cb, workspace=ws, out=Y)
+        torch.cuda.synchronize()
+    reps = 200
+    ms = _event_ms(lambda: orbq.linear_a16(X, rot, wc, wn, cb, workspace=ws, out=Y), reps)
+    Yd = torch.empty_like(Y)
+    ms_dense = _event_ms(lambda: torch.matmul(X, W.t(), out=Yd), reps)
+    nbytes = m * d * bw // 8 + 2 * m + 2 * n * d + 2 * n * m
+    gbps = nbytes / (ms * 1e-3) / 1e9
+    print(json.dumps({"metric": "weight-only (A16) product, FLUX AdaLN modulation shape", "unit": "GB/s",
+                      "value": round(gbps, 1), "higher_is_better": True, "n_gpus": 1, "reps": reps,
+                      "data": "synthetic", "dtype": "bf16",
+                      "config": {"workload": "flux_adaln_a16", "tokens": n, "d": d, "m": m, "bits_w": bw,
+                                 "block": 128},
+                      "us_per_call": round(ms * 1e3, 2), "bytes_per_call": nbytes,
+                      "roofline": {"bound": "hbm", "achieved": round(gbps, 1), "peak": HBM_PEAK_GBPS,
+                                   "unit": "GB/s", "frac": round(gbps / HBM_PEAK_GBPS, 4), "traffic": None},
+                      "context": {"torch_bf16_dense_gemm_us": round(ms_dense * 1e3, 2),
+                                  "dense_weight_bytes": 2 * m * d}}), flush=True)
     return 0
 
 

@@ -74,6 +74,9 @@ _SIGS = {
                                        _P, _P, ctypes.POINTER(_Codebook), _I64, _P, ctypes.c_size_t, ctypes.c_int,
                                        _P, ctypes.c_int, _I64, _P]),
     "orbq_rpbh_flatness": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
+    "orbq_linear_a16_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
+    "orbq_linear_a16": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), _P, _P, ctypes.POINTER(_Codebook),
+                                       _I64, _P, ctypes.c_size_t, _P, ctypes.c_int, _I64, _P]),
     "orbq_rht_passes": (ctypes.c_int32, [ctypes.c_float, ctypes.c_float, _I32, _I32]),
     "orbq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
     "orbq_last_error": (ctypes.c_char_p, []),
@@ -279,6 +282,31 @@ def linear(X, rot: Rotation, cb_a: Codebook, w_codes, w_norms, cb_w: Codebook, e
                                       w_codes.data_ptr(), w_norms.data_ptr(), ctypes.byref(w), m, workspace.data_ptr(),
                                       ws_bytes, code, Y.data_ptr(), yt, Y.stride(0), _stream(torch, X.device)),
                "orbq_linear_act")
+    return Y
+
+
+def linear_a16_workspace_bytes(n: int, d: int, m: int) -> int:
+    return int(load().orbq_linear_a16_workspace_bytes(n, d, m))
+
+
+def linear_a16(X, rot: Rotation, w_codes, w_norms, cb_w: Codebook, out_dtype=None, workspace=None, out=None):
+    """Weight-only product: Y [n, m] from bf16 tokens X [n, d] (rotated, not quantized) and
+    folded weight codes (orbq_linear_a16)."""
+    torch = _torch()
+    _dev_tensor(X, torch.bfloat16, "linear_a16")
+    out_dtype = out_dtype or torch.float32
+    n, d = X.shape
+    m = w_codes.shape[0]
+    need = linear_a16_workspace_bytes(n, d, m)
+    if workspace is None:
+        workspace = torch.empty((max(need, 1),), dtype=torch.uint8, device=X.device)
+    Y = out if out is not None else torch.empty((n, m), dtype=out_dtype, device=X.device)
+    r, w = rot.struct(), cb_w.struct()
+    _check(load().orbq_linear_a16(X.data_ptr(), n, d, X.stride(0), ctypes.byref(r), w_codes.data_ptr(),
+                                  w_norms.data_ptr(), ctypes.byref(w), m, workspace.data_ptr(),
+                                  workspace.numel() * workspace.element_size(), Y.data_ptr(),
+                                  BF16 if Y.dtype == torch.bfloat16 else F32, Y.stride(0), _stream(torch, X.device)),
+           "orbq_linear_a16")
     return Y
 
 

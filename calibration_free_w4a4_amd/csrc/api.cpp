@@ -2,6 +2,7 @@
 // then asynchronous launches of the rpbh_quantize and lut_gemm kernels.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -272,6 +273,69 @@ ORBQ_API int orbq_linear_act(const void* X, int64_t n, int64_t d, int64_t ldx, c
   if (!valid_act(act)) return fail(ORBQ_ERR_INVALID_ARG, "%s: unknown activation %d", what, static_cast<int>(act));
   return linear_impl(X, n, d, ldx, rot, cb_a, eps, w_codes, w_norms, cb_w, m, workspace, ws_bytes, act, Y, y_type,
                      ldy, stream, what);
+}
+
+namespace {
+
+constexpr int64_t kA16Tokens = 16;  // tokens per weight-only launch
+
+size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
+
+size_t a16_ws_bytes(int64_t n, int64_t d, int64_t m) {
+  const int64_t nt = std::min<int64_t>(n, kA16Tokens);
+  int splits = 1, per = 1, rb = 1;
+  orbq::a16_splits(m, d, &splits, &per, &rb);
+  return round256(static_cast<size_t>(nt * d * 4)) + round256(static_cast<size_t>(nt * 4)) +
+         static_cast<size_t>(splits) * static_cast<size_t>(nt) * static_cast<size_t>(m) * 4;
+}
+
+}  // namespace
+
+ORBQ_API size_t orbq_linear_a16_workspace_bytes(int64_t n, int64_t d, int64_t m) {
+  if (n < 0 || d <= 0 || d % 128 || m < 0) return 0;
+  return a16_ws_bytes(std::max<int64_t>(n, 1), d, std::max<int64_t>(m, 1));
+}
+
+ORBQ_API int orbq_linear_a16(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                             const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w, int64_t m,
+                             void* workspace, size_t ws_bytes, void* Y, orbq_dtype y_type, int64_t ldy,
+                             void* stream) {
+  const char* what = "orbq_linear_a16";
+  int s;
+  if ((s = check_dim(d, what))) return s;
+  if (d % 128) return fail(ORBQ_ERR_UNSUPPORTED, "%s: d=%lld not a multiple of 128", what, (long long)d);
+  if ((s = check_rot(rot, d, what))) return s;
+  if ((s = check_codebook(cb_w, d, what))) return s;
+  if (n < 0 || m < 0 || ldx < d || ldy < m) return fail(ORBQ_ERR_INVALID_ARG, "%s: bad n, m, ldx or ldy", what);
+  if (y_type != ORBQ_F32 && y_type != ORBQ_BF16) return fail(ORBQ_ERR_INVALID_ARG, "%s: bad y_type", what);
+  if (n == 0 || m == 0) return ok();
+  if (!X || !w_codes || !w_norms || !Y) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL buffer", what);
+  if (!aligned(X, 16) || (ldx * 2) % 16 || !aligned(w_codes, 16) || !aligned(w_norms, 2) ||
+      !aligned(Y, y_type == ORBQ_BF16 ? 2 : 4))
+    return fail(ORBQ_ERR_ALIGNMENT, "%s: misaligned buffer", what);
+  const size_t need = a16_ws_bytes(n, d, m);
+  if (!workspace || ws_bytes < need)
+    return fail(ORBQ_ERR_WORKSPACE, "%s: workspace %zu bytes < %zu needed", what, ws_bytes, need);
+  if (!aligned(workspace, 256)) return fail(ORBQ_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", what);
+  orbq::DecodeParams dw;
+  orbq::build_decode_params(cb_w->centroids, cb_w->bits, &dw);
+  const int64_t nt_max = std::min<int64_t>(n, kA16Tokens);
+  float* xr = static_cast<float*>(workspace);
+  float* norms = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + round256(static_cast<size_t>(nt_max * d * 4)));
+  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(norms) + round256(static_cast<size_t>(nt_max * 4)));
+  orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs, rot->passes < 1 ? 1 : rot->passes};
+  const int64_t esz = y_type == ORBQ_BF16 ? 2 : 4;
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  for (int64_t t0 = 0; t0 < n; t0 += kA16Tokens) {
+    const int nt = static_cast<int>(std::min<int64_t>(kA16Tokens, n - t0));
+    int e = orbq::launch_rpbh_quantize(orbq::QuantMode::kRotateOnly, static_cast<const uint16_t*>(X) + t0 * ldx, nt,
+                                       ldx, ra, nullptr, 0.0f, nullptr, norms, xr, st);
+    if (e == hipSuccess)
+      e = orbq::launch_a16_gemm(xr, nt, d, w_codes, static_cast<const uint16_t*>(w_norms), dw, m, part,
+                                static_cast<unsigned char*>(Y) + t0 * ldy * esz, y_type == ORBQ_BF16, ldy, st);
+    if (e != hipSuccess) return hip_status(e, what);
+  }
+  return ok();
 }
 
 ORBQ_API int orbq_rpbh_flatness(const void* X, int64_t n, int64_t d, int64_t ldx, float* rho3, float* rhoinf,

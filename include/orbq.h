@@ -193,6 +193,29 @@ int orbq_linear_act(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq
                     const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes,
                     orbq_activation act, void* Y, orbq_dtype y_type, int64_t ldy, void* stream);
 
+/* Weight-only product with bf16 activations (W4A16 and, with 2- or 6-bit weight codes,
+ * W2A16 / W6A16).  The OrbitQuant pages keep the AdaLN activations in BF16 (ai-papers.net
+ * OrbitQuant article, section on AdaLN handling and compression) while the AdaLN modulation
+ * weights go to 4 bits (OrbitQuant summary, "AdaLN Bit-Width Ablation (Figure 6)"); Nunchaku /
+ * SVDQuant in Diffusers (ai-papers.net) names a weight-only 4-bit GEMM for such layers.  The weights are the usual
+ * folded codes; the activations are rotated but not quantized:
+ *   Y[i][j] = r'_j * sum_k bf16((Pi x_i)_k) * bf16(C_w[w_jk])
+ * with Pi x_i computed in fp32 and rounded to bf16 (the matrix cores' input type), fp32
+ * accumulation.  Built for few tokens (modulation vectors, small batches): the weight codes are
+ * streamed once per 16 tokens, so the call is bound by the code bytes.
+ *   X        [device] bf16[n][ldx], 16-byte aligned rows; d a multiple of 128
+ *   rot      rotation the weights were folded with (any passes)
+ *   w_codes, w_norms, cb_w, m   as for orbq_lut_gemm
+ *   workspace [device] >= orbq_linear_a16_workspace_bytes(n, d, m), 256-byte aligned: the
+ *            rotated tokens of a 16-token chunk and the K-split partial sums
+ *   Y        [device] float or bf16 [n][ldy], ldy >= m
+ * Errors as orbq_linear; d % 128 != 0 gives ORBQ_ERR_UNSUPPORTED. */
+size_t orbq_linear_a16_workspace_bytes(int64_t n, int64_t d, int64_t m);
+int orbq_linear_a16(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                    const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w, int64_t m,
+                    void* workspace, size_t ws_bytes, void* Y, orbq_dtype y_type, int64_t ldy,
+                    void* stream);
+
 /* The adaptive check ("Quantizing With Randomized Hadamard Transforms", gist.science,
  * "Method": an O(d) look at the input's l3 norm, for scalar quantization, or its l_inf
  * norm, for vector quantization, decides whether 1, 2 or 3 composed transforms are needed).

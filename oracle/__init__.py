@@ -29,7 +29,7 @@ from .density import log_fd, fd, gaussian_limit_pdf, cell_mass, cell_moment, mea
 from .lloyd_max import lloyd_max, thresholds_midpoint
 from .quantize import argmin_codes, rotate_normalize, quantize_activations, fold_weights, bf16_rne
 from .activation import ACTIVATIONS, activation, gelu_erf, gelu_tanh, lut_gemm_act
-from .linear import (decode_lut_bf16, lut_gemm, orbq_linear, unquantized_fold, to_sign_magnitude,
+from .linear import (decode_lut_bf16, linear_a16, lut_gemm, orbq_linear, unquantized_fold, to_sign_magnitude,
                      from_sign_magnitude, pack_codes, unpack_codes, codes_row_bytes)
 
 __all__ = [
@@ -38,5 +38,5 @@ __all__ = [
     "rotate_normalize", "quantize_activations", "fold_weights", "bf16_rne", "decode_lut_bf16",
     "lut_gemm", "orbq_linear", "unquantized_fold", "to_sign_magnitude", "from_sign_magnitude",
     "pack_codes", "unpack_codes", "codes_row_bytes", "ACTIVATIONS", "activation", "gelu_erf",
-    "gelu_tanh", "lut_gemm_act",
+    "gelu_tanh", "lut_gemm_act", "linear_a16",
 ]

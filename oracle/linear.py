@@ -104,3 +104,18 @@ def unpack_codes(packed, bits: int, d: int) -> np.ndarray:
     else:
         raise ValueError("bits must be 2, 4 or 6")
     return from_sign_magnitude(c, bits)
+
+
+def linear_a16(X, Pi, codes_w, r, cent_w) -> np.ndarray:
+    """Weight-only product with bf16 activations: Y[i, j] = r_j sum_k bf16((Pi x_i)_k) C^_w[w_jk].
+
+    The OrbitQuant pages keep the AdaLN activations in BF16 while its modulation weights are
+    quantized (ai-papers.net article, AdaLN section; picx.dev summary, "AdaLN Bit-Width
+    Ablation (Figure 6)").  The weights are the usual folded codes, so the activations are
+    rotated by the same Pi (the rotations cancel, "Online Activation Quantization") but not
+    normalised or quantized.  Reading: the rotated activations are rounded to bf16 (round to
+    nearest even) once, the precision the product takes its operands in.
+    """
+    A = bf16_rne(rotate(X, Pi))
+    B = decode_lut_bf16(cent_w)[np.asarray(codes_w)]
+    return (A @ B.T) * np.asarray(r, np.float64)[None, :]

@@ -168,6 +168,20 @@ def test_argument_errors_return_before_launch(cb):
     la = lib.orbq_linear_act
     assert la(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, P, P, ctypes.byref(c4), 8, P, need,
               -1, P, 0, 8, None) == -1
+    # weight-only product
+    a16 = lib.orbq_linear_a16
+    wsa = lib.orbq_linear_a16_workspace_bytes(8, d, 8)
+    assert wsa > 0 and lib.orbq_linear_a16_workspace_bytes(8, 192, 8) == 0
+    assert a16(P, 8, d, d, ctypes.byref(rot), P, P + 1, ctypes.byref(c4), 8, P, wsa, P, 0, 8, None) == -3  # w_norms
+    assert a16(P, 8, d, d, ctypes.byref(rot), P + 8, P, ctypes.byref(c4), 8, P, wsa, P, 0, 8, None) == -3  # codes
+    assert a16(P, 8, d, d, ctypes.byref(rot), P, P + 2, ctypes.byref(c4), 8, P, wsa - 1, P, 0, 8, None) == -4
+    assert a16(P, 8, d, d, ctypes.byref(rot), P, P + 2, ctypes.byref(c4), 8, P + 16, wsa, P, 0, 8, None) == -3
+    assert a16(P, 8, d, d, ctypes.byref(rot), P, P + 2, ctypes.byref(c4), 8, P, wsa, P, 0, 4, None) == -1  # ldy
+    assert a16(P, 8, d, d, ctypes.byref(rot), P, P + 2, ctypes.byref(c4), 8, P, wsa, P, 5, 8, None) == -1  # y_type
+    assert a16(P, 0, d, d, ctypes.byref(rot), P, P, ctypes.byref(c4), 8, None, 0, P, 0, 8, None) == 0
+    rot192 = orbq._Rpbh(192, 64, 0x1000, 0x2000)
+    c192, keep192 = _cb_struct(cb(192, 4), 192, 4)
+    assert a16(P, 8, 192, 192, ctypes.byref(rot192), P, P, ctypes.byref(c192), 8, P, 1 << 20, P, 0, 8, None) == -2
     # flatness
     fl = lib.orbq_rpbh_flatness
     assert fl(P, 8, d, d - 8, P, P, None) == -1          # ldx < d

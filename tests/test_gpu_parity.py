@@ -420,6 +420,42 @@ def test_lut_gemm_act_none_and_linear_act(orbq):
             assert torch.equal(G1, G2), (act, dt)
 
 
+@pytest.mark.parametrize("n,d,m,bw,out_bf16", [(2, 3072, 18432, 4, False), (1, 256, 100, 4, False),
+                                               (16, 1536, 1000, 6, True), (37, 3072, 700, 2, False),
+                                               (5, 12288, 3072, 4, True)])
+def test_linear_a16_weight_only(orbq, n, d, m, bw, out_bf16):
+    """orbq_linear_a16 (bf16 activations rotated, weight codes decoded) against the oracle's
+    weight-only product: several token chunks of 16, ragged m, 2/4/6-bit weights, the AdaLN
+    modulation shape (2 x 3072 -> 18432)."""
+    torch = torch_mod()
+    log(f"linear_a16 n={n} d={d} m={m} W{bw} bf16={out_bf16}")
+    h = 64 if d == 256 else 128
+    rot = gpu_rotation(orbq, d, h)
+    cb, c = gpu_codebook(orbq, d, bw)
+    X = workloads.activations(n, d, seed=900 + n, kind="heavy")
+    W = workloads.weights(m, d, 901)
+    wc, wn = orbq.fold_weights(dev_bf16(W), rot, cb)
+    Y = orbq.linear_a16(dev_bf16(X), rot, wc, wn, cb, out_dtype=torch.bfloat16 if out_bf16 else torch.float32)
+    torch.cuda.synchronize()
+    Yg = Y.float().cpu().numpy().astype(np.float64)
+    codes = oracle.unpack_codes(wc.cpu().numpy(), bw, d)
+    r = wn.float().cpu().numpy().astype(np.float64)
+    Pi = dense_pi(d, h)
+    Xf = workloads.f64_from_bf16_bits(X)
+    Yo = oracle.linear_a16(Xf, Pi, codes, r, c)
+    A = oracle.bf16_rne(oracle.rotate(Xf, Pi))
+    den = (np.abs(A) @ np.abs(oracle.decode_lut_bf16(c)[codes]).T) * r[None, :]
+    e = float(np.max(np.abs(Yg - Yo) / den))
+    log(f"  max error / |dot| scale {e:.3g}")
+    assert e <= 2e-3 + (2.0 ** -8 if out_bf16 else 0.0)
+    # against the unquantized product: the weight quantization error only, within the
+    # codebook's distortion bound (sqrt(3) pi / 2) 4^-b per coordinate, with 20 % slack
+    ref = Xf @ workloads.f64_from_bf16_bits(W).T
+    rel = np.linalg.norm(Yg - ref) / np.linalg.norm(ref)
+    log(f"  ||Y - XW^T|| / ||XW^T|| = {rel:.4f}")
+    assert rel < 1.2 * math.sqrt(math.sqrt(3) * math.pi / 2 * 4.0 ** -bw)
+
+
 # ----------------------------------------------------------------- the layer
 def test_linear_equals_quantize_then_gemm(orbq):
     torch = torch_mod()

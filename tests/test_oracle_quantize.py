@@ -150,3 +150,27 @@ def test_packed_layout_hand_example():
     assert list(oracle.pack_codes(np.array([[0, 7, 8, 15]]), 4)[0]) == [0x8F, 0x70]
     assert list(oracle.pack_codes(np.array([[0, 1, 2, 3]]), 2)[0]) == [0x4B]
     assert list(oracle.pack_codes(np.array([[0, 31, 32, 63]]), 6)[0]) == [0x3F, 0x08, 0x7C]
+
+
+def test_linear_a16_rotation_cancels(cb):
+    """Weights built so that their folded rows are exactly r_j C^[codes_j] (W = W' Pi): the
+    weight-only product must reproduce X W^T up to the one bf16 rounding of the rotated
+    activations (2^-9 relative per term).  Forgetting the rotation, or rotating by Pi^T, is off
+    by O(1)."""
+    d, h, bits = 256, 64, 4
+    c = cb(d, bits)
+    perm, signs = workloads.rotation(d)
+    Pi = oracle.rpbh_matrix(d, h, perm, signs)
+    rng = np.random.default_rng(3)
+    codes = rng.integers(0, 16, (9, d))
+    r = rng.uniform(0.5, 2.0, 9)
+    Wp = oracle.decode_lut_bf16(c)[codes] * r[:, None]
+    W = Wp @ Pi
+    X = rng.standard_normal((5, d)) * np.exp(rng.standard_normal(d))
+    Y = oracle.linear_a16(X, Pi, codes, r, c)
+    scale = np.abs(oracle.rotate(X, Pi)) @ np.abs(Wp).T
+    err = np.abs(Y - X @ W.T) / scale
+    assert err.max() <= 2.0 ** -9 * 1.01
+    assert err.max() > 0  # the bf16 rounding is there
+    wrong = (oracle.bf16_rne(X) @ Wp.T)  # no rotation
+    assert np.max(np.abs(wrong - X @ W.T) / scale) > 0.05
