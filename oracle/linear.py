@@ -19,6 +19,7 @@ here independently of the library's code):
       b = 4: code j in byte j//2, bits 4*(j%2) .. +3
       b = 2: code j in byte j//4, bits 2*(j%4) .. +1
       b = 6: code j in the 3-byte little-endian group j//4, bits 6*(j%4) .. +5
+      b = 3: code j in the 3-byte little-endian group j//8, bits 3*(j%8) .. +2
 """
 from __future__ import annotations
 
@@ -86,7 +87,14 @@ def pack_codes(k, bits: int) -> np.ndarray:
         g = c[..., 0] | (c[..., 1] << 6) | (c[..., 2] << 12) | (c[..., 3] << 18)
         out = np.stack([g & 0xFF, (g >> 8) & 0xFF, (g >> 16) & 0xFF], axis=-1)
         return out.reshape(rows, d // 4 * 3).astype(np.uint8)
-    raise ValueError("bits must be 2, 4 or 6")
+    if bits == 3:
+        c = c.reshape(rows, d // 8, 8)
+        g = np.zeros((rows, d // 8), dtype=np.uint32)
+        for i in range(8):
+            g |= c[..., i] << (3 * i)
+        out = np.stack([g & 0xFF, (g >> 8) & 0xFF, (g >> 16) & 0xFF], axis=-1)
+        return out.reshape(rows, d // 8 * 3).astype(np.uint8)
+    raise ValueError("bits must be 2, 3, 4 or 6")
 
 
 def unpack_codes(packed, bits: int, d: int) -> np.ndarray:
@@ -101,8 +109,12 @@ def unpack_codes(packed, bits: int, d: int) -> np.ndarray:
         g3 = p.reshape(rows, d // 4, 3)
         g = g3[..., 0] | (g3[..., 1] << 8) | (g3[..., 2] << 16)
         c = np.stack([(g >> s) & 63 for s in (0, 6, 12, 18)], axis=-1).reshape(rows, d)
+    elif bits == 3:
+        g3 = p.reshape(rows, d // 8, 3)
+        g = g3[..., 0] | (g3[..., 1] << 8) | (g3[..., 2] << 16)
+        c = np.stack([(g >> (3 * i)) & 7 for i in range(8)], axis=-1).reshape(rows, d)
     else:
-        raise ValueError("bits must be 2, 4 or 6")
+        raise ValueError("bits must be 2, 3, 4 or 6")
     return from_sign_magnitude(c, bits)
 
 

@@ -33,7 +33,7 @@ def test_exports_every_declared_symbol():
 
 
 @pytest.mark.parametrize("d,bits", [(256, 4), (3072, 4), (3072, 2), (12288, 4), (1536, 6), (8960, 6),
-                                    (1536, 4), (8960, 4)])
+                                    (1536, 4), (8960, 4), (3072, 3), (256, 3)])
 def test_library_codebook_matches_oracle(d, bits, cb):
     lib_c = orbq.Codebook.lloyd_max(d, bits).centroids
     ref = oracle.lloyd_max(d, bits)

@@ -66,7 +66,7 @@ def test_lloyd_conditions(d, bits, cb):
     assert np.array_equal(c, c64.astype(np.float32))
 
 
-@pytest.mark.parametrize("bits", [1, 2, 4, 6])
+@pytest.mark.parametrize("bits", [1, 2, 3, 4, 6])
 def test_distortion_between_shannon_and_turboquant_bounds(bits):
     d = 3072
     c = oracle.lloyd_max(d, bits)
@@ -94,7 +94,7 @@ def _gaussian_lloyd(bits):
     return c
 
 
-@pytest.mark.parametrize("bits", [2, 4])
+@pytest.mark.parametrize("bits", [2, 3, 4])
 def test_approaches_gaussian_lloyd_max(bits):
     g = _gaussian_lloyd(bits)
     gaps = []

@@ -132,7 +132,7 @@ def test_end_to_end_error_tracks_codebook_distortion(bits, cb):
     assert 0.5 * math.sqrt(2 * D) < err < 2.0 * math.sqrt(2 * D), (err, math.sqrt(2 * D))
 
 
-@pytest.mark.parametrize("bits", [2, 4, 6])
+@pytest.mark.parametrize("bits", [2, 3, 4, 6])
 def test_pack_unpack_roundtrip_and_layout(bits):
     rng = np.random.default_rng(bits)
     k = rng.integers(0, 1 << bits, (3, 64))
@@ -150,6 +150,9 @@ def test_packed_layout_hand_example():
     assert list(oracle.pack_codes(np.array([[0, 7, 8, 15]]), 4)[0]) == [0x8F, 0x70]
     assert list(oracle.pack_codes(np.array([[0, 1, 2, 3]]), 2)[0]) == [0x4B]
     assert list(oracle.pack_codes(np.array([[0, 31, 32, 63]]), 6)[0]) == [0x3F, 0x08, 0x7C]
+    # 3-bit [0, 3, 4, 7, 1, 2, 5, 6] -> sign-magnitude [7, 4, 0, 3, 6, 5, 1, 2] -> 24-bit group
+    # 0b010_001_101_110_011_000_100_111 = 0x46E627 -> bytes 0x27, 0xE6, 0x46
+    assert list(oracle.pack_codes(np.array([[0, 3, 4, 7, 1, 2, 5, 6]]), 3)[0]) == [0x27, 0xE6, 0x46]
 
 
 def test_linear_a16_rotation_cancels(cb):
