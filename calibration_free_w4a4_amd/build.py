@@ -20,7 +20,8 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liborbq.so")
 ARCH = os.environ.get("ORBQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["api.cpp", "codebook.cpp", "rpbh_quantize.hip", "lut_gemm.hip", "flatness.hip"]
+SOURCES = ["lut_gemm_a4.hip", "lut_gemm_a6.hip", "lut_gemm_a2.hip", "lut_gemm_a3.hip", "rpbh_quantize.hip",
+           "a16_gemm.hip", "lut_gemm.hip", "flatness.hip", "api.cpp", "codebook.cpp"]
 
 
 def hipcc() -> str:
@@ -46,7 +47,7 @@ def _compile(src: str) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=4) as ex:
+    with ThreadPoolExecutor(max_workers=min(8, os.cpu_count() or 4)) as ex:
         objs = list(ex.map(_compile, SOURCES))
     tmp = LIB + ".tmp"
     cmd = [hipcc(), f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp] + objs

@@ -34,12 +34,12 @@ int ok() {
 
 bool aligned(const void* p, size_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
 
-bool supported_bits(int b) { return b == 2 || b == 4 || b == 6; }
+bool supported_bits(int b) { return b == 2 || b == 3 || b == 4 || b == 6; }
 
 int check_codebook(const orbq_codebook* cb, int64_t d, const char* what) {
   if (!cb) return fail(ORBQ_ERR_INVALID_ARG, "%s: codebook is NULL", what);
   if (!cb->centroids) return fail(ORBQ_ERR_INVALID_ARG, "%s: codebook centroids are NULL", what);
-  if (!supported_bits(cb->bits)) return fail(ORBQ_ERR_UNSUPPORTED, "%s: codebook bits %d not in {2,4,6}", what, cb->bits);
+  if (!supported_bits(cb->bits)) return fail(ORBQ_ERR_UNSUPPORTED, "%s: codebook bits %d not in {2,3,4,6}", what, cb->bits);
   if (d >= 0 && cb->d != d) return fail(ORBQ_ERR_INVALID_ARG, "%s: codebook d=%d but d=%lld", what, cb->d, (long long)d);
   const int n = 1 << cb->bits;
   for (int k = 0; k < n; ++k) {
@@ -176,6 +176,8 @@ int gemm_checks(const uint8_t* x_codes, const float* x_norms, const orbq_codeboo
   if (y_type != ORBQ_F32 && y_type != ORBQ_BF16) return fail(ORBQ_ERR_INVALID_ARG, "%s: bad y_type", what);
   if ((s = check_codebook(cb_a, d, what))) return s;
   if ((s = check_codebook(cb_w, d, what))) return s;
+  if ((cb_a->bits == 3) != (cb_w->bits == 3))
+    return fail(ORBQ_ERR_UNSUPPORTED, "%s: 3-bit codes pair only with 3-bit codes (W3A3)", what);
   if (n == 0 || m == 0) return ORBQ_OK;
   if ((check_x && (!x_codes || !x_norms)) || !w_codes || !w_norms || !Y)
     return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL buffer", what);

@@ -434,6 +434,19 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
 #pragma unroll
         for (int i = 0; i < kE; ++i) w |= quantize_one(y[i] * inv_s, tbl, J) << (2 * i);
         __builtin_amdgcn_raw_buffer_store_b32(static_cast<int>(w), codes_rs, off, 0, 0);
+      } else if constexpr (BITS == 3) {
+        // 48 bits at a 2-byte aligned offset (6 bytes per lane): three 16-bit stores
+        uint32_t w[2] = {0, 0};
+#pragma unroll
+        for (int i = 0; i < kE; ++i) {
+          const uint32_t c = quantize_one(y[i] * inv_s, tbl, J);
+          const int bit = 3 * i, wi = bit >> 5, sh = bit & 31;
+          w[wi] |= c << sh;
+          if (sh > 29) w[wi + 1] |= c >> (32 - sh);
+        }
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(w[0] & 0xFFFFu), codes_rs, off, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(w[0] >> 16), codes_rs, off + 2u, 0, 0);
+        __builtin_amdgcn_raw_buffer_store_b16(static_cast<short>(w[1] & 0xFFFFu), codes_rs, off + 4u, 0, 0);
       } else {
         uint32_t w[3] = {0, 0, 0};
 #pragma unroll
@@ -461,6 +474,7 @@ __global__ void k_quantize_t(const float* t, int64_t count, QuantParams qp, uint
   __shared__ float2 tbl_all[2 * kMaxTableHalf];
   switch (qp.bits) {
     case 2: build_table<2>(qp, tbl_all, threadIdx.x, blockDim.x); break;
+    case 3: build_table<3>(qp, tbl_all, threadIdx.x, blockDim.x); break;
     case 4: build_table<4>(qp, tbl_all, threadIdx.x, blockDim.x); break;
     default: build_table<6>(qp, tbl_all, threadIdx.x, blockDim.x); break;
   }
@@ -500,6 +514,7 @@ hipError_t launch_perm(int bits, const QuantKernelArgs& a, int threads, size_t l
   if constexpr (MODE == QuantMode::kRotateOnly) return launch_typed<H, 4, MODE, PERM, MULTI>(a, threads, lds, st);
   switch (bits) {
     case 2: return launch_typed<H, 2, MODE, PERM, MULTI>(a, threads, lds, st);
+    case 3: return launch_typed<H, 3, MODE, PERM, MULTI>(a, threads, lds, st);
     case 4: return launch_typed<H, 4, MODE, PERM, MULTI>(a, threads, lds, st);
     default: return launch_typed<H, 6, MODE, PERM, MULTI>(a, threads, lds, st);
   }

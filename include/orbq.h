@@ -32,6 +32,7 @@
  *        bits = 4: code j in byte j/2, bits 4*(j%2)..+3
  *        bits = 2: code j in byte j/4, bits 2*(j%4)..+1
  *        bits = 6: code j in the 3-byte little-endian group j/4, bits 6*(j%4)..+5
+ *        bits = 3: code j in the 3-byte little-endian group j/8, bits 3*(j%8)..+2
  *   - The product decodes each centroid to bf16 (round to nearest even), multiplies in
  *     bf16 with fp32 accumulation, and scales by s_i (fp32) and r'_j (bf16) in fp32.
  *
@@ -45,7 +46,8 @@
  * clamped into range (garbage in, garbage out, no out-of-bounds access).
  *
  * Supported shapes: block a power of two in [64, 1024]; d a multiple of block and at most 16384;
- * activation bits and weight bits each in {2, 4, 6}.  n or m equal to 0 is a no-op.
+ * activation bits and weight bits each in {2, 3, 4, 6}, 3-bit codes in the product only with
+ * 3-bit codes (W3A3; the OrbitQuant summary's 3-bit setting).  n or m equal to 0 is a no-op.
  * Alignment: bf16 matrices and code buffers 16-byte aligned with row pitches that
  * are multiples of 16 bytes; norm arrays 4-byte (fp32) or 2-byte (bf16) aligned;
  * Y 16-byte aligned with a row pitch that is a multiple of 16 bytes.

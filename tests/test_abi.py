@@ -88,7 +88,7 @@ def test_codebook_validate(cb):
     nan = good.copy(); nan[5] = np.nan
     s, keep = _cb_struct(nan, 256, 4)
     assert lib.orbq_codebook_validate(ctypes.byref(s)) == -6
-    s, keep = _cb_struct(cb(256, 4), 256, 3)
+    s, keep = _cb_struct(np.linspace(-1, 1, 32), 256, 5)
     assert lib.orbq_codebook_validate(ctypes.byref(s)) == -2
 
 
@@ -100,7 +100,8 @@ def test_sizes():
     assert lib.orbq_codes_row_bytes(3, 2) == 0
     ws = lib.orbq_linear_workspace_bytes(4608, 3072, 4)
     assert ws == ((4608 * 1536 + 255) // 256) * 256 + 4608 * 4
-    assert lib.orbq_linear_workspace_bytes(10, 3072, 3) == 0
+    assert lib.orbq_linear_workspace_bytes(10, 3072, 5) == 0
+    assert lib.orbq_linear_workspace_bytes(10, 3072, 3) == ((10 * 1152 + 255) // 256) * 256 + 40
 
 
 def test_status_strings():
@@ -132,8 +133,11 @@ def test_argument_errors_return_before_launch(cb):
     assert q(P, 8, d, d, ctypes.byref(rot_mis), ctypes.byref(c4), 1e-8, P, P, None) == -3      # perm alignment
     c4d, keep = _cb_struct(cb(d, 4), 512, 4)
     assert q(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4d), 1e-8, P, P, None) == -1         # codebook d
-    c3, keep3 = _cb_struct(np.linspace(-1, 1, 8), d, 3)
-    assert q(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c3), 1e-8, P, P, None) == -2          # bits
+    c5, keep5 = _cb_struct(np.linspace(-1, 1, 32), d, 5)
+    assert q(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c5), 1e-8, P, P, None) == -2          # bits
+    c3, keep3 = _cb_struct(cb(d, 3), d, 3)
+    g0 = lib.orbq_lut_gemm
+    assert g0(P, P, ctypes.byref(c3), P, P, ctypes.byref(c4), 8, 8, d, P, 0, 8, None) == -2      # 3-bit with 4-bit
     assert "ld" in lib.orbq_last_error().decode() or lib.orbq_last_error()
     # n == 0 is a no-op that succeeds without touching the device
     assert q(None, 0, d, d, ctypes.byref(rot), ctypes.byref(c4), 1e-8, None, None, None) == 0

@@ -44,7 +44,8 @@ def gpu_rotation(orbq, d, h):
 
 
 # ----------------------------------------------------------------- decision rule
-@pytest.mark.parametrize("d,bits", [(256, 4), (3072, 4), (3072, 2), (1536, 6), (8960, 6), (12288, 4)])
+@pytest.mark.parametrize("d,bits", [(256, 4), (3072, 4), (3072, 2), (1536, 6), (8960, 6), (12288, 4), (3072, 3),
+                                    (256, 3)])
 def test_quantize_t_exact(orbq, d, bits):
     """The kernels' decision on given fp32 t equals the oracle's exact argmin, bit for bit,
     including every boundary, its fp32 neighbours, zeros, denormals and far tails."""
@@ -267,6 +268,30 @@ def test_fold_weights_sampled(orbq, name):
     _quant_case(orbq, name, weights=True, sample=lambda n: _sample_rows(n, 40, 1))
 
 
+@pytest.mark.parametrize("d,h,n,weights", [(3072, 128, 333, False), (3072, 128, 97, True), (256, 64, 70, False)])
+def test_quantize_3bit(orbq, d, h, n, weights):
+    """3-bit codes (W3A3): 16 codes per lane in 6 bytes (three 16-bit stores at 2-byte aligned
+    offsets), every coordinate against the oracle; ragged last group."""
+    log(f"quantize 3-bit d={d} n={n} weights={weights}")
+    rot = gpu_rotation(orbq, d, h)
+    cb, c = gpu_codebook(orbq, d, 3)
+    src = workloads.weights(n, d, 1301) if weights else workloads.activations(n, d, seed=1300, kind="heavy")
+    if weights:
+        codes, norms = orbq.fold_weights(dev_bf16(src), rot, cb)
+        norms = norms.float()
+    else:
+        codes, norms = orbq.rpbh_quantize(dev_bf16(src), rot, cb)
+    assert codes.shape == (n, d * 3 // 8)
+    k_ref, s_ref, T_ref = oracle.quantize_activations(workloads.f64_from_bf16_bits(src), dense_pi(d, h), c)
+    check_codes(oracle.unpack_codes(codes.cpu().numpy(), 3, d), k_ref, T_ref, c, "3-bit")
+    got = norms.cpu().numpy().astype(np.float64)
+    if weights:
+        r_ref = oracle.bf16_rne(s_ref)
+        assert np.all(np.abs(got - r_ref) <= 2.0 ** (np.floor(np.log2(r_ref)) - 7))
+    else:
+        assert np.max(np.abs(got - s_ref) / s_ref) < 1e-6
+
+
 # ----------------------------------------------------------------- product
 def _gemm_case(orbq, n, m, d, ba, bw, out_bf16=False, seed=7, sample=None):
     torch = torch_mod()
@@ -299,7 +324,7 @@ def _gemm_case(orbq, n, m, d, ba, bw, out_bf16=False, seed=7, sample=None):
     return e
 
 
-@pytest.mark.parametrize("ba,bw", [(4, 4), (4, 2), (6, 4), (2, 2), (6, 6), (2, 6)])
+@pytest.mark.parametrize("ba,bw", [(4, 4), (4, 2), (6, 4), (2, 2), (6, 6), (2, 6), (3, 3)])
 def test_lut_gemm_tiny_all_bit_pairs(orbq, ba, bw):
     assert _gemm_case(orbq, 64, 256, 256, ba, bw) < 1e-5
 
@@ -310,6 +335,13 @@ def test_lut_gemm_ragged(orbq, out_bf16):
     _gemm_case(orbq, 300, 520, 3072, 4, 4, out_bf16=out_bf16)
 
 
+@pytest.mark.parametrize("n,m,d", [(300, 520, 3072), (70, 200, 192), (1000, 2100, 1536)])
+def test_lut_gemm_w3a3(orbq, n, m, d):
+    """3-bit x 3-bit: units of 8 codes at 3-byte offsets (8-byte loads from the aligned word
+    below), ragged tiles, odd K-tile counts."""
+    _gemm_case(orbq, n, m, d, 3, 3)
+
+
 @pytest.mark.parametrize("ba,bw", [(4, 4), (6, 4), (2, 6)])
 @pytest.mark.parametrize("d", [192, 320, 64])
 def test_lut_gemm_odd_k_tile_count(orbq, ba, bw, d):
@@ -318,7 +350,7 @@ def test_lut_gemm_odd_k_tile_count(orbq, ba, bw, d):
 
 
 @pytest.mark.parametrize("ba,bw,out_bf16,d", [(4, 4, True, 512), (4, 4, False, 576), (6, 4, True, 512),
-                                               (4, 2, True, 576)])
+                                               (4, 2, True, 576), (3, 3, True, 576)])
 def test_lut_gemm_wide_tiles_ragged(orbq, ba, bw, out_bf16, d):
     """Shapes for which the host picks 384 x 192 workgroup tiles, with partial tiles on both axes
     (last token tile 284 of 384 rows, last weight tile 136 of 192 rows) and even or odd K-tile
@@ -420,7 +452,7 @@ def test_lut_gemm_act_none_and_linear_act(orbq):
             assert torch.equal(G1, G2), (act, dt)
 
 
-@pytest.mark.parametrize("n,d,m,bw,out_bf16", [(2, 3072, 18432, 4, False), (1, 256, 100, 4, False),
+@pytest.mark.parametrize("n,d,m,bw,out_bf16", [(2, 3072, 18432, 4, False), (1, 256, 100, 4, False), (3, 3072, 777, 3, True),
                                                (16, 1536, 1000, 6, True), (37, 3072, 700, 2, False),
                                                (5, 12288, 3072, 4, True)])
 def test_linear_a16_weight_only(orbq, n, d, m, bw, out_bf16):
@@ -484,6 +516,32 @@ def test_linear_equals_quantize_then_gemm(orbq):
     rel = np.linalg.norm(Y.cpu().numpy() - ref) / np.linalg.norm(ref)
     log(f"  ||Y - XW^T|| / ||XW^T|| = {rel:.4f}")
     assert rel < 0.3
+
+
+def test_linear_w3a3_end_to_end(orbq):
+    """W3A3 layer: orbq_linear equals quantize-then-gemm bit for bit, and matches the oracle
+    chain (codes may flip at boundaries) within 2e-3 of the |dot| scale."""
+    torch = torch_mod()
+    d, h, n, m = 3072, 128, 130, 400
+    rot = gpu_rotation(orbq, d, h)
+    cb, c = gpu_codebook(orbq, d, 3)
+    X = workloads.activations(n, d, seed=1400, kind="heavy")
+    W = workloads.weights(m, d, 1401)
+    dX = dev_bf16(X)
+    wc, wn = orbq.fold_weights(dev_bf16(W), rot, cb)
+    Y = orbq.linear(dX, rot, cb, wc, wn, cb)
+    xc, xs = orbq.rpbh_quantize(dX, rot, cb)
+    Y2 = orbq.lut_gemm(xc, xs, cb, wc, wn, cb, d)
+    torch.cuda.synchronize()
+    assert torch.equal(Y, Y2)
+    Pi = dense_pi(d, h)
+    kw, r, _, _ = oracle.fold_weights(workloads.f64_from_bf16_bits(W), Pi, c)
+    Yo, kx, s = oracle.orbq_linear(workloads.f64_from_bf16_bits(X), Pi, c, kw, r, c)
+    lut = oracle.decode_lut_bf16(c)
+    den = (np.abs(lut[kx]) @ np.abs(lut[kw]).T) * s[:, None] * r[None, :]
+    e = np.max(np.abs(Y.cpu().numpy() - Yo) / den)
+    log(f"  W3A3 linear vs oracle chain: {e:.3g}")
+    assert e < 2e-3
 
 
 # ----------------------------------------------------------------- edge cases
