@@ -241,7 +241,7 @@ def main() -> int:
         copy_gbps = 2 * src.numel() / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
         del src, dst, A, B
 
-    gemm_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "lut_gemm.hip")
+    gemm_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "lut_gemm_kernel.h")
     quant_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "rpbh_quantize.hip")
     g_tflops = flops / (g_ms * 1e-3) / 1e12
     q_gbps = q_bytes / (q_ms * 1e-3) / 1e9

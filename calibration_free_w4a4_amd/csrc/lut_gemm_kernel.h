@@ -25,8 +25,11 @@
 //   * LDS: two stages of [BM + BN][64] bf16, 128-byte rows whose 16-byte chunks are xor-swizzled
 //     by (row >> 1) & 7; the MFMA fragment reads (32 rows at one chunk) and the staging stores
 //     (8 rows x 8 chunks per wave) are free of bank conflicts.  One barrier per K tile.
-//   * schedule: inside a K tile every second MFMA is followed by half of one unit's decode (and
-//     its LDS store), so the decode of the next K tile runs in the shadow of the matrix cores.
+//   * schedule: a K tile is 4 k-steps of TI x TJ MFMAs.  The decode of the next K tile (half a
+//     unit after two of every three MFMAs, with its LDS store) fills the first three k-steps;
+//     the fragment reads of the next k-step are spread over the first MFMAs of the current one.
+//     The K tile's one barrier sits before its last k-step, whose MFMAs then cover the reads of
+//     the next K tile's first fragments: no wave starts a K tile waiting for LDS.
 //   * epilogue: Y = act(acc * s_i * r'_j) in fp32, stored as fp32 or bf16 (round to nearest
 //     even); act is the identity or GELU (tanh or erf form), the activation an MLP applies
 //     between its up- and down-projection (Nunchaku / SVDQuant in Diffusers, ai-papers.net,
@@ -417,20 +420,28 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
       f.fb[j] = *reinterpret_cast<const bf16x8_t*>(smem + b_off[ks] + buf * C::SB + j * (32 * kRow));
   };
 
-  // one K tile: MFMAs on stage `buf`, with the decode of set `s` into stage 1 - buf in their
-  // shadow (half a unit after every second MFMA)
-  auto ktile = [&](int buf, Set& s) {
-    Frags f[2];
-    read_frags(f[0], buf, 0);
+  // one K tile: MFMAs on stage `buf` (its first fragments already in f[0]); the decode of set
+  // `s` into stage 1 - buf runs in the shadow of the first three k-steps, then one barrier, and
+  // the last k-step's MFMAs cover the reads of the next tile's first fragments
+  auto ktile = [&](int buf, Set& s, Frags (&f)[2]) {
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks < 3) read_frags(f[(ks + 1) & 1], buf, ks + 1);
+      if (ks == 3) __syncthreads();
 #pragma unroll
       for (int p = 0; p < C::NM; ++p) {
         const int i = p / C::TJ, j = p % C::TJ;
         acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f[ks & 1].fa[i], f[ks & 1].fb[j], acc[i][j], 0, 0, 0);
+        if (p < C::TI + C::TJ) {
+          Frags& g2 = f[(ks + 1) & 1];
+          const int kn = ks < 3 ? ks + 1 : 0;
+          const int bn = ks < 3 ? buf : 1 - buf;
+          if (p < C::TI)
+            g2.fa[p] = *reinterpret_cast<const bf16x8_t*>(smem + a_off[kn] + bn * C::SA + p * (32 * kRow));
+          else
+            g2.fb[p - C::TI] = *reinterpret_cast<const bf16x8_t*>(smem + b_off[kn] + bn * C::SB + (p - C::TI) * (32 * kRow));
+        }
         const int q = ks * C::NM + p;
-        if (q & 1) half_step(s, 1 - buf, q >> 1);
+        if (ks < 3 && (q % 3) != 2) half_step(s, 1 - buf, 2 * (q / 3) + (q % 3));
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -453,13 +464,13 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
   }
   __syncthreads();
 
+  Frags f[2];
+  read_frags(f[0], 0, 0);
   for (int v = 0; v < nv; v += 2) {
     load_set(s0, v + 2);
-    ktile(0, s1);  // MFMAs on tile v, decode of tile v + 1
-    __syncthreads();
+    ktile(0, s1, f);  // MFMAs on tile v, decode of tile v + 1
     load_set(s1, v + 3);
-    ktile(1, s0);  // MFMAs on tile v + 1, decode of tile v + 2
-    __syncthreads();
+    ktile(1, s0, f);  // MFMAs on tile v + 1, decode of tile v + 2
   }
 
   // ---- epilogue: D[row][col] of a 32x32 tile: col = lane % 32, row = 8*(r/4) + 4*(lane/32) + r%4
