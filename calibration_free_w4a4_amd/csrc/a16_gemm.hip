@@ -15,6 +15,17 @@ namespace {
 // them 8 at a time in four MFMAs.  The k order inside each 8 (0,2,4,6,1,3,5,7, the decoders'
 // order) is applied to x' as well.  Partial sums of each split go to a workspace; a second
 // kernel adds the splits and applies r'.
+// A buffer resource from wave-uniform values, forced into scalar registers: the compiler keeps
+// values derived from 64-bit compares and selects in VGPRs, which would wrap every load that
+// uses the resource in a waterfall loop.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t b = reinterpret_cast<uint64_t>(base);
+  const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b));
+  const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(b >> 32));
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((static_cast<uint64_t>(hi) << 32) | lo), 0,
+                                           __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
+}
+
 constexpr int kA16Waves = 4;
 constexpr int kA16Rows = 64;                  // weight rows per wave
 constexpr int kA16SS = 128;                   // codes per super-step
@@ -112,11 +123,10 @@ __global__ __launch_bounds__(64 * kA16Waves) void k_a16_partial(A16Args a) {
   const int64_t row_base = (static_cast<int64_t>(rblk) * kA16Waves + wave) * kA16Rows;
 
   // x' rows past nt read as zero; code rows past m read as zero (never stored)
-  const __amdgpu_buffer_rsrc_t xs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(a.xr), 0, a.xr_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t xs = uniform_rsrc(a.xr, a.xr_bytes);
   const int64_t rows_left = a.m - row_base;
   const uint32_t wc_bytes = rows_left <= 0 ? 0u : static_cast<uint32_t>(min<int64_t>(rows_left, kA16Rows) * a.rb);
-  const __amdgpu_buffer_rsrc_t ws =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(a.wc + (rows_left > 0 ? row_base * a.rb : 0)), 0, wc_bytes, kBufWord3);
+  const __amdgpu_buffer_rsrc_t ws = uniform_rsrc(a.wc + (rows_left > 0 ? row_base * a.rb : 0), wc_bytes);
   const uint32_t xoff = static_cast<uint32_t>(m16 < a.nt ? m16 * a.d * 4 : 0x7FFFFFF0) ;
   f32x4_t acc[4];
 #pragma unroll

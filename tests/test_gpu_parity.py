@@ -452,17 +452,22 @@ def test_lut_gemm_act_none_and_linear_act(orbq):
             assert torch.equal(G1, G2), (act, dt)
 
 
-@pytest.mark.parametrize("n,d,m,bw,out_bf16", [(2, 3072, 18432, 4, False), (1, 256, 100, 4, False), (3, 3072, 777, 3, True),
-                                               (16, 1536, 1000, 6, True), (37, 3072, 700, 2, False),
-                                               (5, 12288, 3072, 4, True)])
-def test_linear_a16_weight_only(orbq, n, d, m, bw, out_bf16):
+@pytest.mark.parametrize("n,d,m,bw,out_bf16,passes", [
+    (2, 3072, 18432, 4, False, 1), (1, 256, 100, 4, False, 1), (3, 3072, 777, 3, True, 1),
+    (1, 12288, 3072, 4, False, 1), (5, 3072, 1000, 6, True, 1), (16, 1536, 1000, 6, True, 1),
+    (37, 3072, 700, 2, False, 1), (5, 12288, 3072, 4, True, 1), (2, 3072, 600, 4, False, 2)])
+def test_linear_a16_weight_only(orbq, n, d, m, bw, out_bf16, passes):
     """orbq_linear_a16 (bf16 activations rotated, weight codes decoded) against the oracle's
-    weight-only product: several token chunks of 16, ragged m, 2/4/6-bit weights, the AdaLN
-    modulation shape (2 x 3072 -> 18432)."""
+    weight-only product: 16-token chunks, a composed rotation, ragged m, 2/3/4/6-bit weights, the
+    AdaLN modulation shape (2 x 3072 -> 18432)."""
     torch = torch_mod()
-    log(f"linear_a16 n={n} d={d} m={m} W{bw} bf16={out_bf16}")
+    log(f"linear_a16 n={n} d={d} m={m} W{bw} bf16={out_bf16} passes={passes}")
     h = 64 if d == 256 else 128
-    rot = gpu_rotation(orbq, d, h)
+    if passes == 1:
+        rot = gpu_rotation(orbq, d, h)
+    else:
+        pp, sp = workloads.rotation_passes(d, passes)
+        rot = orbq.Rotation.create(d, h, pp, sp, passes=passes)
     cb, c = gpu_codebook(orbq, d, bw)
     X = workloads.activations(n, d, seed=900 + n, kind="heavy")
     W = workloads.weights(m, d, 901)
@@ -472,7 +477,7 @@ def test_linear_a16_weight_only(orbq, n, d, m, bw, out_bf16):
     Yg = Y.float().cpu().numpy().astype(np.float64)
     codes = oracle.unpack_codes(wc.cpu().numpy(), bw, d)
     r = wn.float().cpu().numpy().astype(np.float64)
-    Pi = dense_pi(d, h)
+    Pi = dense_pi(d, h) if passes == 1 else oracle.rpbh_composed(d, h, pp, sp, passes)
     Xf = workloads.f64_from_bf16_bits(X)
     Yo = oracle.linear_a16(Xf, Pi, codes, r, c)
     A = oracle.bf16_rne(oracle.rotate(Xf, Pi))
