@@ -189,7 +189,7 @@ def main() -> int:
     q_bytes = L.n * (2 * L.d + L.d * L.bits_a // 8 + 4)
     value = flops / (ms_step * 1e-3) / 1e12
 
-    linear_ms = q_cold_ms = ref_gemm_tflops = copy_gbps = float("nan")
+    linear_ms = q_cold_ms = ref_gemm_tflops = copy_gbps = copy_same_us = copy_same_step_us = float("nan")
     if not args.no_extras:
         # ---- the same layer through the single orbq_linear entry point (cross-check)
         for _ in range(3):
@@ -239,7 +239,25 @@ def main() -> int:
         e1.record()
         torch.cuda.synchronize()
         copy_gbps = 2 * src.numel() / (e0.elapsed_time(e1) / 10 * 1e-3) / 1e9
-        del src, dst, A, B
+        # a device copy that moves the bytes rpbh_quantize moves (q_bytes / 2 read, as many
+        # written), timed the same ways: back to back, and between GEMM launches
+        half = q_bytes // 2
+        csrc, cdst = src[:half], dst[:half]
+        e0.record()
+        for _ in range(100):
+            cdst.copy_(csrc)
+        e1.record()
+        torch.cuda.synchronize()
+        copy_same_us = e0.elapsed_time(e1) / 100 * 1e3
+        cev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(20)]
+        for ea, eb in cev:
+            gemm()
+            ea.record()
+            cdst.copy_(csrc)
+            eb.record()
+        torch.cuda.synchronize()
+        copy_same_step_us = statistics.mean(ea.elapsed_time(eb) for ea, eb in cev) * 1e3
+        del src, dst, A, B, csrc, cdst
 
     gemm_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "lut_gemm_kernel.h")
     quant_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "rpbh_quantize.hip")
@@ -271,7 +289,9 @@ def main() -> int:
                           "frac": round(q_gbps / HBM_PEAK_GBPS, 4),
                           "traffic": _traffic(quant_src, "rpbh_quantize", name)},
         "context": {"torch_bf16_matmul_TFLOPs": _r(ref_gemm_tflops, 1),
-                    "torch_copy_GBps": _r(copy_gbps, 1)},
+                    "torch_copy_GBps": _r(copy_gbps, 1),
+                    "copy_of_rpbh_bytes_us": _r(copy_same_us, 2),
+                    "copy_of_rpbh_bytes_in_step_us": _r(copy_same_step_us, 2)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L, X_bits, W_bits, perm, signs, args.cpu_tokens, args.cpu_weights)
