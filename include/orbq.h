@@ -3,8 +3,11 @@
  *
  * Pages cited: "OrbitQuant: Data-Agnostic Quantization for Image and Video Diffusion
  * Transformers" (summary page on picx.dev; cited as "OrbitQuant summary" with its section
- * titles) and the TurboQuant slide deck ("TurboQuant: Online Vector Quantization with
- * Near-optimal Distortion Rate", docswell; cited by slide number "Page. N").
+ * titles), the TurboQuant slide deck ("TurboQuant: Online Vector Quantization with
+ * Near-optimal Distortion Rate", docswell; cited by slide number "Page. N"), "Quantizing With
+ * Randomized Hadamard Transforms" (gist.science; composed rotations and the flatness check),
+ * the ai-papers.net OrbitQuant article (AdaLN kept at BF16 activations) and the ai-papers.net
+ * article on Nunchaku / SVDQuant in Diffusers (GELU fused with the MLP; weight-only kernels).
  *
  * What the library computes (OrbitQuant summary, picx.dev, "Methodology"):
  *   offline  "Offline Weight Quantization": W' = W Pi^T, r'_i = ||w'_i||, codes of
@@ -38,7 +41,7 @@
  *
  * Memory: every buffer is owned by the caller.  Pointers marked [device] are HIP device
  * pointers, [host] are host pointers.  The library allocates no device memory: the
- * workspace of orbq_linear comes from the caller.  Calls are asynchronous on `stream`
+ * workspaces of orbq_linear, orbq_linear_act and orbq_linear_a16 come from the caller.  Calls are asynchronous on `stream`
  * (a hipStream_t; NULL = the default stream) and re-entrant; argument errors are
  * detected on the host before anything is launched and are returned synchronously.
  * Device faults surface at the caller's next synchronisation.  Device arrays (perm,
