@@ -63,9 +63,9 @@ struct CodesA16<2> {
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     w = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
   }
-  __device__ __forceinline__ uint4 get(int s, const Tab4&, const void* lut) const {
-    const uint32_t x = (s < 2 ? w.x : w.y) >> (16 * (s & 1));
-    return decode2(x, static_cast<const uint2*>(lut));
+  __device__ __forceinline__ uint4 get(int s, const Tab4& t, const void*) const {
+    const uint32_t x = ((s < 2 ? w.x : w.y) >> (16 * (s & 1))) & 0xFFFFu;
+    return decode2_b(decode2_a(x, t), t);
   }
 };
 
@@ -106,10 +106,10 @@ struct CodesA16<6> {
 
 template <int BW>
 __global__ __launch_bounds__(64 * kA16Waves) void k_a16_partial(A16Args a) {
-  __shared__ __align__(16) unsigned char lut[BW == 6 ? 4096 * 4 : BW == 2 ? 256 * 8 : BW == 3 ? 64 * 4 : 16];
+  __shared__ __align__(16) unsigned char lut[BW == 6 ? 4096 * 4 : BW == 3 ? 64 * 4 : 16];
   __shared__ uint16_t mags[32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if constexpr (BW != 4) {
+  if constexpr (needs_lut(BW)) {
     if (tid < 32) mags[tid] = a.mag[tid];
     __syncthreads();
     build_lut<BW, 64 * kA16Waves>(mags, lut, tid);

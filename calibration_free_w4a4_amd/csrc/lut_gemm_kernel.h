@@ -19,8 +19,9 @@
 //     thread decodes the same number of units.  Code rows are read with buffer loads (rows past
 //     the end read as zero and are never stored), two K tiles ahead in registers.
 //   * decode of 4-bit codes: v_perm_b32 byte lookups into the 8 bf16 magnitudes (held in four
-//     registers) plus the sign bit; 2-bit codes use a 256-entry LDS table per code byte, 6-bit
-//     codes a 4096-entry LDS table per code pair.  Every decoder writes the 8 values of a
+//     registers) plus the sign bit; 2-bit codes the same into the 4 signed values (two
+//     registers); 3-bit codes use a 64-entry LDS table per code pair, 6-bit codes a
+//     4096-entry one.  Every decoder writes the 8 values of a
 //     16-byte chunk in the order k = 0,2,4,6,1,3,5,7, so A and B agree on k.
 //   * LDS: two stages of [BM + BN][64] bf16, 128-byte rows whose 16-byte chunks are xor-swizzled
 //     by (row >> 1) & 7; the MFMA fragment reads (32 rows at one chunk) and the staging stores
@@ -117,11 +118,32 @@ __device__ __forceinline__ uint4 decode4_b(uint32_t X, Half4 h) {
   return r;
 }
 
-// 2-bit: 16 bits hold 8 codes; lut2[b] = {(e0, e2), (e1, e3)} of code byte b
-__device__ __forceinline__ uint4 decode2(uint32_t X16, const uint2* lut2) {
-  const uint2 p0 = lut2[X16 & 0xFF];
-  const uint2 p1 = lut2[(X16 >> 8) & 0xFF];
-  return make_uint4(p0.x, p1.x, p0.y, p1.y);
+// 2-bit, in two halves, by v_perm_b32 byte lookups into the 4 signed bf16 values (their low
+// bytes in t.lt_lo, their high bytes in t.ht_lo).  16 bits hold 8 codes; u = x | x << 12 has
+// e0, e4, e2, e6 in the low two bits of bytes 0..3 and e1, e5, e3, e7 two bits above them.
+struct Half2 {
+  uint32_t le, he, od;
+};
+
+__device__ __forceinline__ Half2 decode2_a(uint32_t x16, const Tab4& t) {
+  const uint32_t u = (x16 << 12) | x16;
+  const uint32_t ev = u & 0x03030303u;
+  Half2 h;
+  h.od = (u >> 2) & 0x03030303u;
+  h.le = __builtin_amdgcn_perm(t.lt_lo, t.lt_lo, ev);
+  h.he = __builtin_amdgcn_perm(t.ht_lo, t.ht_lo, ev);
+  return h;
+}
+
+__device__ __forceinline__ uint4 decode2_b(Half2 h, const Tab4& t) {
+  const uint32_t lo = __builtin_amdgcn_perm(t.lt_lo, t.lt_lo, h.od);
+  const uint32_t ho = __builtin_amdgcn_perm(t.ht_lo, t.ht_lo, h.od);
+  uint4 r;
+  r.x = __builtin_amdgcn_perm(h.he, h.le, 0x06020400u);  // (e0, e2)
+  r.y = __builtin_amdgcn_perm(h.he, h.le, 0x07030501u);  // (e4, e6)
+  r.z = __builtin_amdgcn_perm(ho, lo, 0x06020400u);      // (e1, e3)
+  r.w = __builtin_amdgcn_perm(ho, lo, 0x07030501u);      // (e5, e7)
+  return r;
 }
 
 // 6-bit: 48 bits (lo 32 + hi 16) hold 8 codes; lut6[i] = (bf16 c(i & 63), bf16 c(i >> 6))
@@ -157,18 +179,12 @@ __device__ __forceinline__ uint16_t mag_signed(const uint16_t* mag, uint32_t cod
   return static_cast<uint16_t>(mag[code & (half - 1)] | ((code & half) ? 0x8000u : 0u));
 }
 
-constexpr int lut_bytes_dev(int bits) { return bits == 2 ? 256 * 8 : bits == 6 ? 4096 * 4 : bits == 3 ? 64 * 4 : 0; }
+constexpr int lut_bytes_dev(int bits) { return bits == 6 ? 4096 * 4 : bits == 3 ? 64 * 4 : 0; }
+constexpr bool needs_lut(int bits) { return bits == 3 || bits == 6; }
 
 template <int BITS, int NT = kThreads>
 __device__ __forceinline__ void build_lut(const uint16_t* mag, unsigned char* p, int tid) {
-  if constexpr (BITS == 2) {
-    uint2* l = reinterpret_cast<uint2*>(p);
-    for (int b = tid; b < 256; b += NT) {
-      const uint32_t c0 = mag_signed(mag, b & 3, 2), c1 = mag_signed(mag, (b >> 2) & 3, 2);
-      const uint32_t c2 = mag_signed(mag, (b >> 4) & 3, 2), c3 = mag_signed(mag, (b >> 6) & 3, 2);
-      l[b] = make_uint2(c0 | (c2 << 16), c1 | (c3 << 16));
-    }
-  } else if constexpr (BITS == 6) {
+  if constexpr (BITS == 6) {
     uint32_t* l = reinterpret_cast<uint32_t*>(p);
     for (int i = tid; i < 4096; i += NT)
       l[i] = mag_signed(mag, i & 63, 6) | (static_cast<uint32_t>(mag_signed(mag, i >> 6, 6)) << 16);
@@ -201,13 +217,12 @@ template <>
 struct Unit<2> {
   static constexpr int kStep = KT / 4;
   uint32_t w;
+  Half2 h;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     w = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
   }
-  __device__ __forceinline__ void first(const Tab4&, const void*) {}
-  __device__ __forceinline__ uint4 second(const Tab4&, const void* lut) const {
-    return decode2(w, static_cast<const uint2*>(lut));
-  }
+  __device__ __forceinline__ void first(const Tab4& t, const void*) { h = decode2_a(w, t); }
+  __device__ __forceinline__ uint4 second(const Tab4& t, const void*) const { return decode2_b(h, t); }
   static __device__ __forceinline__ uint32_t col_bytes(uint32_t c) { return 2 * c; }
 };
 
@@ -303,11 +318,11 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
   const int64_t row0 = static_cast<int64_t>(tn) * BM;  // token rows
   const int64_t col0 = static_cast<int64_t>(tm) * BN;  // weight rows
 
-  // decode tables for 2- and 6-bit codes, built from the magnitudes (staged through the first
+  // decode tables for 3- and 6-bit codes, built from the magnitudes (staged through the first
   // bytes of the B region, which the first K tile overwrites only after the next barrier)
   unsigned char* lut_a = lut;
   unsigned char* lut_w = lut + lut_bytes_dev(BA);
-  if constexpr (BA != 4 || BW != 4) {  // (also 3-bit)
+  if constexpr (needs_lut(BA) || needs_lut(BW)) {
     uint16_t* mags = reinterpret_cast<uint16_t*>(smem + 2 * C::SA);
 #pragma unroll
     for (int r = 0; r < 32; ++r) {
@@ -587,6 +602,12 @@ inline void tab4(const DecodeParams& dp, uint32_t* lt_lo, uint32_t* lt_hi, uint3
     for (int r = 0; r < 8; ++r) {
       l[r >> 2] |= static_cast<uint32_t>(dp.mag[r] & 0xFF) << (8 * (r & 3));
       h[r >> 2] |= static_cast<uint32_t>(dp.mag[r] >> 8) << (8 * (r & 3));
+    }
+  } else if (dp.bits == 2) {  // the 4 signed values: code q = magnitude q & 1, sign q & 2
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t v = dp.mag[q & 1] | ((q & 2) ? 0x8000u : 0u);
+      l[0] |= (v & 0xFF) << (8 * q);
+      h[0] |= (v >> 8) << (8 * q);
     }
   }
   *lt_lo = l[0];
