@@ -77,11 +77,11 @@ struct CodesA16<3> {
     a = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
     b = __builtin_amdgcn_raw_buffer_load_b32(rs, off + 8, 0, 0);
   }
-  __device__ __forceinline__ uint4 get(int s, const Tab4&, const void* lut) const {
+  __device__ __forceinline__ uint4 get(int s, const Tab4& t, const void*) const {
     // 24 bits per 8 codes: s = 0 -> a.x [0, 24), 1 -> (a.x, a.y) [24, 48), 2 -> (a.y, b) [48, 72), 3 -> b [72, 96)
     const uint32_t x = s == 0 ? a.x : s == 1 ? __builtin_amdgcn_alignbit(a.y, a.x, 24)
                      : s == 2 ? __builtin_amdgcn_alignbit(b, a.y, 16) : (b >> 8);
-    return decode3(x, static_cast<const uint32_t*>(lut));
+    return decode3_b(decode3_a(x, t), t);
   }
 };
 
@@ -106,7 +106,7 @@ struct CodesA16<6> {
 
 template <int BW>
 __global__ __launch_bounds__(64 * kA16Waves) void k_a16_partial(A16Args a) {
-  __shared__ __align__(16) unsigned char lut[BW == 6 ? 4096 * 4 : BW == 3 ? 64 * 4 : 16];
+  __shared__ __align__(16) unsigned char lut[BW == 6 ? 4096 * 4 : 16];
   __shared__ uint16_t mags[32];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if constexpr (needs_lut(BW)) {

@@ -6,7 +6,7 @@ namespace orbq {
 namespace lg {
 namespace {
 
-size_t lut_bytes(int bits) { return bits == 6 ? 4096 * 4 : bits == 3 ? 64 * 4 : 0; }
+size_t lut_bytes(int bits) { return bits == 6 ? 4096 * 4 : 0; }
 
 int device_cus() {
   static thread_local int cached_dev = -1, cached_cus = 0;

@@ -19,9 +19,8 @@
 //     thread decodes the same number of units.  Code rows are read with buffer loads (rows past
 //     the end read as zero and are never stored), two K tiles ahead in registers.
 //   * decode of 4-bit codes: v_perm_b32 byte lookups into the 8 bf16 magnitudes (held in four
-//     registers) plus the sign bit; 2-bit codes the same into the 4 signed values (two
-//     registers); 3-bit codes use a 64-entry LDS table per code pair, 6-bit codes a
-//     4096-entry one.  Every decoder writes the 8 values of a
+//     registers) plus the sign bit; 2- and 3-bit codes the same into the 4 or 8 signed values;
+//     6-bit codes use a 4096-entry LDS table per code pair.  Every decoder writes the 8 values of a
 //     16-byte chunk in the order k = 0,2,4,6,1,3,5,7, so A and B agree on k.
 //   * LDS: two stages of [BM + BN][64] bf16, 128-byte rows whose 16-byte chunks are xor-swizzled
 //     by (row >> 1) & 7; the MFMA fragment reads (32 rows at one chunk) and the staging stores
@@ -160,17 +159,32 @@ __device__ __forceinline__ uint4 decode6(uint32_t lo, uint32_t hi, const uint32_
   return r;
 }
 
-// 3-bit: 24 bits hold 8 codes; lut3[i] = (bf16 c(i & 7), bf16 c(i >> 3)) for a 6-bit code pair
-__device__ __forceinline__ uint4 decode3(uint32_t x, const uint32_t* lut3) {
-  const uint32_t p01 = lut3[x & 63];
-  const uint32_t p23 = lut3[(x >> 6) & 63];
-  const uint32_t p45 = lut3[(x >> 12) & 63];
-  const uint32_t p67 = lut3[(x >> 18) & 63];
+// 3-bit, in two halves, by v_perm_b32 byte lookups into the 8 signed bf16 values (low bytes in
+// t.lt_lo / t.lt_hi, high bytes in t.ht_lo / t.ht_hi).  The low 24 bits of x hold 8 codes (bits
+// above are ignored); y has e0..e3 in its low half and e4..e7 in its high half, 12 bits each,
+// from which e0, e2, e4, e6 (then e1, e3, e5, e7) are moved to the low bits of bytes 0..3.
+struct Half3 {
+  uint32_t y, le, he;
+};
+
+__device__ __forceinline__ Half3 decode3_a(uint32_t x, const Tab4& t) {
+  Half3 h;
+  h.y = (x & 0xFFFu) | ((x << 4) & ~0xFFFu);  // bits 12..15 and 28..31 are never read
+  const uint32_t ev = (h.y & 0x00070007u) | ((h.y << 2) & 0x07000700u);
+  h.le = __builtin_amdgcn_perm(t.lt_hi, t.lt_lo, ev);
+  h.he = __builtin_amdgcn_perm(t.ht_hi, t.ht_lo, ev);
+  return h;
+}
+
+__device__ __forceinline__ uint4 decode3_b(const Half3& h, const Tab4& t) {
+  const uint32_t od = ((h.y >> 3) & 0x00070007u) | ((h.y >> 1) & 0x07000700u);
+  const uint32_t lo = __builtin_amdgcn_perm(t.lt_hi, t.lt_lo, od);
+  const uint32_t ho = __builtin_amdgcn_perm(t.ht_hi, t.ht_lo, od);
   uint4 r;
-  r.x = __builtin_amdgcn_perm(p23, p01, 0x05040100u);  // (e0, e2)
-  r.y = __builtin_amdgcn_perm(p67, p45, 0x05040100u);  // (e4, e6)
-  r.z = __builtin_amdgcn_perm(p23, p01, 0x07060302u);  // (e1, e3)
-  r.w = __builtin_amdgcn_perm(p67, p45, 0x07060302u);  // (e5, e7)
+  r.x = __builtin_amdgcn_perm(h.he, h.le, 0x05010400u);  // (e0, e2)
+  r.y = __builtin_amdgcn_perm(h.he, h.le, 0x07030602u);  // (e4, e6)
+  r.z = __builtin_amdgcn_perm(ho, lo, 0x05010400u);      // (e1, e3)
+  r.w = __builtin_amdgcn_perm(ho, lo, 0x07030602u);      // (e5, e7)
   return r;
 }
 
@@ -179,8 +193,8 @@ __device__ __forceinline__ uint16_t mag_signed(const uint16_t* mag, uint32_t cod
   return static_cast<uint16_t>(mag[code & (half - 1)] | ((code & half) ? 0x8000u : 0u));
 }
 
-constexpr int lut_bytes_dev(int bits) { return bits == 6 ? 4096 * 4 : bits == 3 ? 64 * 4 : 0; }
-constexpr bool needs_lut(int bits) { return bits == 3 || bits == 6; }
+constexpr int lut_bytes_dev(int bits) { return bits == 6 ? 4096 * 4 : 0; }
+constexpr bool needs_lut(int bits) { return bits == 6; }
 
 template <int BITS, int NT = kThreads>
 __device__ __forceinline__ void build_lut(const uint16_t* mag, unsigned char* p, int tid) {
@@ -188,10 +202,6 @@ __device__ __forceinline__ void build_lut(const uint16_t* mag, unsigned char* p,
     uint32_t* l = reinterpret_cast<uint32_t*>(p);
     for (int i = tid; i < 4096; i += NT)
       l[i] = mag_signed(mag, i & 63, 6) | (static_cast<uint32_t>(mag_signed(mag, i >> 6, 6)) << 16);
-  } else if constexpr (BITS == 3) {
-    uint32_t* l = reinterpret_cast<uint32_t*>(p);
-    for (int i = tid; i < 64; i += NT)
-      l[i] = mag_signed(mag, i & 7, 3) | (static_cast<uint32_t>(mag_signed(mag, i >> 3, 3)) << 16);
   }
 }
 
@@ -231,13 +241,14 @@ struct Unit<3> {
   static constexpr int kStep = KT * 3 / 8;  // 24 bytes per K tile of a row
   v2u_t w;        // 8 bytes read from a 4-byte aligned offset; the unit starts 0..3 bytes in
   uint32_t sh;    // 8 * (3 c mod 4): bit offset of the unit in w
+  Half3 h;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     w = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
   }
-  __device__ __forceinline__ void first(const Tab4&, const void*) {}
-  __device__ __forceinline__ uint4 second(const Tab4&, const void* lut) const {
-    return decode3(__builtin_amdgcn_alignbit(w.y, w.x, sh), static_cast<const uint32_t*>(lut));
+  __device__ __forceinline__ void first(const Tab4& t, const void*) {
+    h = decode3_a(__builtin_amdgcn_alignbit(w.y, w.x, sh), t);
   }
+  __device__ __forceinline__ uint4 second(const Tab4& t, const void*) const { return decode3_b(h, t); }
   static __device__ __forceinline__ uint32_t col_bytes(uint32_t c) { return (3 * c) & ~3u; }
 };
 
@@ -318,7 +329,7 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
   const int64_t row0 = static_cast<int64_t>(tn) * BM;  // token rows
   const int64_t col0 = static_cast<int64_t>(tm) * BN;  // weight rows
 
-  // decode tables for 3- and 6-bit codes, built from the magnitudes (staged through the first
+  // decode table for 6-bit codes, built from the magnitudes (staged through the first
   // bytes of the B region, which the first K tile overwrites only after the next barrier)
   unsigned char* lut_a = lut;
   unsigned char* lut_w = lut + lut_bytes_dev(BA);
@@ -603,11 +614,12 @@ inline void tab4(const DecodeParams& dp, uint32_t* lt_lo, uint32_t* lt_hi, uint3
       l[r >> 2] |= static_cast<uint32_t>(dp.mag[r] & 0xFF) << (8 * (r & 3));
       h[r >> 2] |= static_cast<uint32_t>(dp.mag[r] >> 8) << (8 * (r & 3));
     }
-  } else if (dp.bits == 2) {  // the 4 signed values: code q = magnitude q & 1, sign q & 2
-    for (int q = 0; q < 4; ++q) {
-      const uint32_t v = dp.mag[q & 1] | ((q & 2) ? 0x8000u : 0u);
-      l[0] |= (v & 0xFF) << (8 * q);
-      h[0] |= (v >> 8) << (8 * q);
+  } else if (dp.bits == 2 || dp.bits == 3) {  // the signed values: code q = sign bit, then magnitude
+    const int half = 1 << (dp.bits - 1);
+    for (int q = 0; q < 2 * half; ++q) {
+      const uint32_t v = dp.mag[q & (half - 1)] | ((q & half) ? 0x8000u : 0u);
+      l[q >> 2] |= (v & 0xFF) << (8 * (q & 3));
+      h[q >> 2] |= (v >> 8) << (8 * (q & 3));
     }
   }
   *lt_lo = l[0];
