@@ -145,18 +145,33 @@ __device__ __forceinline__ uint4 decode2_b(Half2 h, const Tab4& t) {
   return r;
 }
 
-// 6-bit: 48 bits (lo 32 + hi 16) hold 8 codes; lut6[i] = (bf16 c(i & 63), bf16 c(i >> 6))
-__device__ __forceinline__ uint4 decode6(uint32_t lo, uint32_t hi, const uint32_t* lut6) {
-  const uint32_t p01 = lut6[lo & 0xFFF];
-  const uint32_t p23 = lut6[(lo >> 12) & 0xFFF];
-  const uint32_t p45 = lut6[((lo >> 24) | (hi << 8)) & 0xFFF];
-  const uint32_t p67 = lut6[(hi >> 4) & 0xFFF];
+// 6-bit, in two halves: (1) the four lookups of code pairs in lut6[i] = (bf16 c(i & 63),
+// bf16 c(i >> 6)), issued a half-step before (2) their use, so that the wait for them does not
+// also wait for the fragment reads issued in between; 48 bits (lo 32 + hi 16) hold 8 codes.
+struct Half6 {
+  uint32_t p01, p23, p45, p67;
+};
+
+__device__ __forceinline__ Half6 decode6_a(uint32_t lo, uint32_t hi, const uint32_t* lut6) {
+  Half6 h;
+  h.p01 = lut6[lo & 0xFFF];
+  h.p23 = lut6[(lo >> 12) & 0xFFF];
+  h.p45 = lut6[((lo >> 24) | (hi << 8)) & 0xFFF];
+  h.p67 = lut6[(hi >> 4) & 0xFFF];
+  return h;
+}
+
+__device__ __forceinline__ uint4 decode6_b(const Half6& h) {
   uint4 r;
-  r.x = __builtin_amdgcn_perm(p23, p01, 0x05040100u);  // (e0, e2)
-  r.y = __builtin_amdgcn_perm(p67, p45, 0x05040100u);  // (e4, e6)
-  r.z = __builtin_amdgcn_perm(p23, p01, 0x07060302u);  // (e1, e3)
-  r.w = __builtin_amdgcn_perm(p67, p45, 0x07060302u);  // (e5, e7)
+  r.x = __builtin_amdgcn_perm(h.p23, h.p01, 0x05040100u);  // (e0, e2)
+  r.y = __builtin_amdgcn_perm(h.p67, h.p45, 0x05040100u);  // (e4, e6)
+  r.z = __builtin_amdgcn_perm(h.p23, h.p01, 0x07060302u);  // (e1, e3)
+  r.w = __builtin_amdgcn_perm(h.p67, h.p45, 0x07060302u);  // (e5, e7)
   return r;
+}
+
+__device__ __forceinline__ uint4 decode6(uint32_t lo, uint32_t hi, const uint32_t* lut6) {
+  return decode6_b(decode6_a(lo, hi, lut6));
 }
 
 // 3-bit, in two halves, by v_perm_b32 byte lookups into the 8 signed bf16 values (low bytes in
@@ -257,15 +272,16 @@ struct Unit<6> {
   static constexpr int kStep = KT * 6 / 8;
   v2u_t w;        // 8 bytes read from a 4-byte aligned offset; the unit starts 0 or 2 bytes in
   uint32_t sh;    // 0 or 16: bit offset of the unit in w
+  Half6 h;
   __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t rs, uint32_t off) {
     w = __builtin_amdgcn_raw_buffer_load_b64(rs, off, 0, 0);
   }
-  __device__ __forceinline__ void first(const Tab4&, const void*) {}
-  __device__ __forceinline__ uint4 second(const Tab4&, const void* lut) const {
+  __device__ __forceinline__ void first(const Tab4&, const void* lut) {
     const uint32_t lo = __builtin_amdgcn_alignbit(w.y, w.x, sh);
     const uint32_t hi = (w.y >> sh) & 0xFFFFu;
-    return decode6(lo, hi, static_cast<const uint32_t*>(lut));
+    h = decode6_a(lo, hi, static_cast<const uint32_t*>(lut));
   }
+  __device__ __forceinline__ uint4 second(const Tab4&, const void*) const { return decode6_b(h); }
   static __device__ __forceinline__ uint32_t col_bytes(uint32_t c) { return (6 * c) & ~3u; }
 };
 
