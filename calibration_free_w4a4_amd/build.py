@@ -20,7 +20,7 @@ BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "liborbq.so")
 ARCH = os.environ.get("ORBQ_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["lut_gemm_a4.hip", "lut_gemm_a6.hip", "lut_gemm_a2.hip", "lut_gemm_a3.hip", "rpbh_quantize.hip",
+SOURCES = ["lut_gemm_a4.hip", "lut_gemm_a6.hip", "lut_gemm_abf.hip", "lut_gemm_a2.hip", "lut_gemm_a3.hip", "rpbh_quantize.hip",
            "a16_gemm.hip", "lut_gemm.hip", "flatness.hip", "api.cpp", "codebook.cpp"]
 
 

@@ -101,6 +101,13 @@ int quantize_rows(orbq::QuantMode mode, const void* X, int64_t n, int64_t d, int
   if (!aligned(norms, norm_align)) return fail(ORBQ_ERR_ALIGNMENT, "%s: norms misaligned", what);
   orbq::QuantParams qp;
   if ((s = quant_params(cb, &qp, what))) return s;
+  if (mode == orbq::QuantMode::kDecoded) {  // the bf16 centroid of each sign-magnitude code, as the product decodes it
+    orbq::DecodeParams dp;
+    orbq::build_decode_params(cb->centroids, cb->bits, &dp);
+    const int half = 1 << (cb->bits - 1);
+    for (int q = 0; q < 2 * half; ++q)
+      qp.vals[q] = static_cast<uint16_t>(dp.mag[q & (half - 1)] | ((q & half) ? 0x8000u : 0u));
+  }
   orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs, rot->passes < 1 ? 1 : rot->passes};
   const int e = orbq::launch_rpbh_quantize(mode, static_cast<const uint16_t*>(X), n, ld, ra, &qp, eps, codes, norms,
                                            nullptr, static_cast<hipStream_t>(stream));
@@ -201,8 +208,19 @@ int gemm_launch(const uint8_t* x_codes, const float* x_norms, const orbq_codeboo
 
 bool valid_act(int act) { return act == ORBQ_ACT_NONE || act == ORBQ_ACT_GELU_TANH || act == ORBQ_ACT_GELU_ERF; }
 
+// The layer's activation operand in its workspace: packed codes, or for 6-bit activations the
+// codes' bf16 centroids (16 bits per coordinate), which the product stages without decoding.
+// The product decodes each activation row once per column tile of 192 or 256 weight rows, while
+// the centroids cost rpbh_quantize 1.25 more bytes per coordinate to write and the product as
+// many more to read; measured on MI355X the centroids win from about 7 column tiles on (W4A6:
+// m = 8960 takes 1.0 ms against 1.8 ms, m = 1536 1.22 ms against 1.21 ms).  The workspace is
+// sized for the centroids either way.
+constexpr int32_t kDecodedBits = 6;
+constexpr int64_t kDecodedMinM = 2048;
+
 size_t ws_codes_bytes(int64_t n, int64_t d, int32_t bits) {
-  return (static_cast<size_t>(n) * static_cast<size_t>(d * bits / 8) + 255) & ~size_t(255);
+  const int64_t row = bits == kDecodedBits ? d * 2 : d * bits / 8;
+  return (static_cast<size_t>(n) * static_cast<size_t>(row) + 255) & ~size_t(255);
 }
 
 }  // namespace
@@ -252,6 +270,17 @@ int linear_impl(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpb
   if (!aligned(workspace, 256)) return fail(ORBQ_ERR_ALIGNMENT, "%s: workspace must be 256-byte aligned", what);
   uint8_t* codes = static_cast<uint8_t*>(workspace);
   float* norms = reinterpret_cast<float*>(codes + ws_codes_bytes(n, d, cb_a->bits));
+  if (cb_a->bits == kDecodedBits && m >= kDecodedMinM) {
+    // 6-bit activations: rpbh_quantize writes the bf16 centroids, the product stages them directly
+    s = quantize_rows(orbq::QuantMode::kDecoded, X, n, d, ldx, rot, cb_a, eps, codes, norms, 4, stream, what);
+    if (s) return s;
+    orbq::DecodeParams da{}, dw;
+    da.bits = 16;
+    orbq::build_decode_params(cb_w->centroids, cb_w->bits, &dw);
+    const int e = orbq::launch_lut_gemm(codes, norms, da, w_codes, static_cast<const uint16_t*>(w_norms), dw, n, m, d,
+                                        Y, y_type == ORBQ_BF16, ldy, act, static_cast<hipStream_t>(stream));
+    return hip_status(e, what);
+  }
   s = quantize_rows(orbq::QuantMode::kActivations, X, n, d, ldx, rot, cb_a, eps, codes, norms, 4, stream, what);
   if (s) return s;
   return gemm_launch(codes, norms, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, act, stream, what);

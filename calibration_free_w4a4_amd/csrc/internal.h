@@ -28,6 +28,7 @@ struct QuantParams {
   int32_t bits;
   float thr_gt[kMaxPosBoundaries + 1];
   float thr_ge[kMaxPosBoundaries + 1];
+  uint16_t vals[64];  // bf16 of the signed centroid of each code (QuantMode::kDecoded only)
 };
 
 // Host: builds QuantParams from an ascending, antisymmetric fp32 codebook.
@@ -54,7 +55,10 @@ struct RotArgs {
   int32_t passes;  // composed passes (1..3); perm and signs hold passes * d entries
 };
 
-enum class QuantMode { kActivations, kWeights, kRotateOnly };
+// kDecoded: activations written as the bf16 centroids of their codes (qp.vals), [n][d] bf16 with
+// the 8 values of each aligned group of 8 positions in the order 0,2,4,6,1,3,5,7 (the order in
+// which the product stages its operands), for a product that stages them without decoding.
+enum class QuantMode { kActivations, kWeights, kRotateOnly, kDecoded };
 
 int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t ldx, const RotArgs& rot,
                          const QuantParams* qp, float eps, uint8_t* codes, void* norms, float* x_rot,

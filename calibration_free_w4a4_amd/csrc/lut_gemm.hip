@@ -87,6 +87,7 @@ int launch_lut_gemm(const uint8_t* x_codes, const float* x_norms, const DecodePa
         case 2: e = launch_gemm_a2(dw.bits, cfg, y_bf16 != 0, b, grid, lds, stream); break;
         case 3: e = launch_gemm_a3(dw.bits, cfg, y_bf16 != 0, b, grid, lds, stream); break;
         case 4: e = launch_gemm_a4(dw.bits, cfg, y_bf16 != 0, b, grid, lds, stream); break;
+        case 16: e = launch_gemm_abf(dw.bits, cfg, y_bf16 != 0, b, grid, lds, stream); break;
         default: e = launch_gemm_a6(dw.bits, cfg, y_bf16 != 0, b, grid, lds, stream); break;
       }
     }

@@ -20,7 +20,8 @@
 //     the end read as zero and are never stored), two K tiles ahead in registers.
 //   * decode of 4-bit codes: v_perm_b32 byte lookups into the 8 bf16 magnitudes (held in four
 //     registers) plus the sign bit; 2- and 3-bit codes the same into the 4 or 8 signed values;
-//     6-bit codes use a 4096-entry LDS table per code pair.  Every decoder writes the 8 values of a
+//     6-bit codes use a 4096-entry LDS table per code pair.  Activations already decoded to bf16
+//     centroids (the layer's path for 6-bit activations) are staged by direct-to-LDS loads.  Every decoder writes the 8 values of a
 //     16-byte chunk in the order k = 0,2,4,6,1,3,5,7, so A and B agree on k.
 //   * LDS: two stages of [BM + BN][64] bf16, 128-byte rows whose 16-byte chunks are xor-swizzled
 //     by (row >> 1) & 7; the MFMA fragment reads (32 rows at one chunk) and the staging stores
@@ -285,6 +286,25 @@ struct Unit<6> {
   static __device__ __forceinline__ uint32_t col_bytes(uint32_t c) { return (6 * c) & ~3u; }
 };
 
+// bf16 operand rows (activations already decoded to their centroids, in the staged k order):
+// staged by direct-to-LDS loads, nothing held in registers and nothing to decode
+template <>
+struct Unit<16> {
+  static constexpr int kStep = KT * 2;
+  __device__ __forceinline__ void load(__amdgpu_buffer_rsrc_t, uint32_t) {}
+  __device__ __forceinline__ void first(const Tab4&, const void*) {}
+  __device__ __forceinline__ uint4 second(const Tab4&, const void*) const { return make_uint4(0, 0, 0, 0); }
+  static __device__ __forceinline__ uint32_t col_bytes(uint32_t c) { return 16 * c; }
+};
+
+// 16 bytes per lane from a buffer straight into LDS (buffer_load_dwordx4 ... lds): lane l's bytes
+// land at lds + 16 l.  The LDS base goes through M0 and must be wave-uniform.
+__device__ __forceinline__ void lds_dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds, uint32_t voff) {
+#if __HIP_DEVICE_COMPILE__
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, voff, 0, 0, 0);
+#endif
+}
+
 // ----------------------------------------------------------------------------- activations
 // GELU, tanh form: x/2 (1 + tanh(u)), u = sqrt(2/pi) (x + 0.044715 x^3), rewritten as the
 // logistic x / (1 + exp(-2u)) = x / (1 + 2^-z), z = x (k0 + k1 x^2), k0 = 2 sqrt(2/pi) log2(e),
@@ -400,6 +420,19 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
 #pragma unroll
     for (int i = 0; i < C::U - C::UA; ++i) s.ub[i].load(rw, woff0 + 64u * i * wrow);
   };
+  // bf16 A rows: each wave's 64 lanes fill 8 whole staged rows (1 KB) per load; lane l takes the
+  // 16-byte chunk that belongs in slot l % 8 of row l / 8 (the rows' chunk swizzle)
+  auto load_a_lds = [&](int v, int stage) {
+    if constexpr (BA == 16) {
+      const auto rx = rsrc(xbase, xrem, real_tile(v), KT * 2);
+      const uint32_t lrow = (tid >> 3) & 7, slot = tid & 7;
+#pragma unroll
+      for (int i = 0; i < C::UA; ++i) {
+        const uint32_t row = 64u * i + 8u * wave + lrow;
+        lds_dma16(rx, smem + stage * C::SA + (64 * i + 8 * wave) * kRow, row * xrow + ((slot ^ swz(row)) << 4));
+      }
+    }
+  };
   if constexpr (BA == 6 || BA == 3) {
     const uint32_t sh = BA == 6 ? (c & 1) * 16 : 8 * ((3 * c) & 3);
 #pragma unroll
@@ -415,6 +448,7 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
   auto half_step = [&](Set& s, int buf, int h) {
     const int u = h >> 1;
     if (u < C::UA) {
+      if constexpr (BA == 16) return;  // staged by the direct loads
       if ((h & 1) == 0) s.ua[u].first(ta, lut_a);
       else {
         const uint4 v = s.ua[u].second(ta, lut_a);
@@ -465,10 +499,16 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
   // one K tile: MFMAs on stage `buf` (its first fragments already in f[0]); the decode of set
   // `s` into stage 1 - buf runs in the shadow of the first three k-steps, then one barrier, and
   // the last k-step's MFMAs cover the reads of the next tile's first fragments
-  auto ktile = [&](int buf, Set& s, Frags (&f)[2]) {
+  auto ktile = [&](int buf, Set& s, Frags (&f)[2], int v) {
+    if constexpr (BA == 16) {  // bf16 A of the next K tile, straight into its stage
+      if (v + 1 < nv) load_a_lds(v + 1, 1 - buf);
+    }
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      if (ks == 3) __syncthreads();
+      if (ks == 3) {
+        if constexpr (BA == 16) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): this wave's direct loads landed
+        __syncthreads();
+      }
 #pragma unroll
       for (int p = 0; p < C::NM; ++p) {
         const int i = p / C::TJ, j = p % C::TJ;
@@ -493,6 +533,9 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
   // is the padding tile of an odd tile count)
   load_set(s0, 0);
   load_set(s1, 1);
+  if constexpr (BA == 16) {
+    if (!odd) load_a_lds(0, 0);
+  }
   if (odd) {
 #pragma unroll
     for (int u = 0; u < C::UA; ++u)
@@ -504,15 +547,16 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
 #pragma unroll
     for (int h = 0; h < 2 * C::U; ++h) half_step(s0, 0, h);
   }
+  if constexpr (BA == 16) __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
   __syncthreads();
 
   Frags f[2];
   read_frags(f[0], 0, 0);
   for (int v = 0; v < nv; v += 2) {
     load_set(s0, v + 2);
-    ktile(0, s1, f);  // MFMAs on tile v, decode of tile v + 1
+    ktile(0, s1, f, v);  // MFMAs on tile v, decode of tile v + 1
     load_set(s1, v + 3);
-    ktile(1, s0, f);  // MFMAs on tile v + 1, decode of tile v + 2
+    ktile(1, s0, f, v + 1);  // MFMAs on tile v + 1, decode of tile v + 2
   }
 
   // ---- epilogue: D[row][col] of a 32x32 tile: col = lane % 32, row = 8*(r/4) + 4*(lane/32) + r%4
@@ -649,6 +693,7 @@ hipError_t launch_gemm_a2(int bw, int cfg, bool out_bf16, const GemmArgs& a, int
 hipError_t launch_gemm_a3(int bw, int cfg, bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st);
 hipError_t launch_gemm_a4(int bw, int cfg, bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st);
 hipError_t launch_gemm_a6(int bw, int cfg, bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st);
+hipError_t launch_gemm_abf(int bw, int cfg, bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st);
 
 }  // namespace lg
 }  // namespace orbq

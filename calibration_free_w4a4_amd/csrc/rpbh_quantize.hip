@@ -114,7 +114,7 @@ __device__ __forceinline__ uint16_t bf16_rne_dev(float x) {
 // (threshold, base code); the code is base + (|t'| > threshold).  The loop over the BITS-bit
 // codebook's positive boundaries is unrolled so that the thresholds are read from the kernel
 // arguments once (scalar loads with constant offsets), and the body has no branches.
-template <int BITS>
+template <int BITS, bool DEC = false>
 __device__ void build_table(const QuantParams& qp, float2* tbl, int tid, int nthreads) {
   constexpr int NB = (1 << (BITS - 1)) - 1, HALF = 1 << (BITS - 1);
   const int J = qp.J;
@@ -131,7 +131,12 @@ __device__ void build_table(const QuantParams& qp, float2* tbl, int tid, int nth
       base += below ? 1 : 0;
       thr = (!below && b < hi) ? b : thr;
     }
-    tbl[e] = make_float2(thr, __builtin_bit_cast(float, base));
+    if constexpr (DEC) {  // the bf16 centroids of codes base and base + 1 (base + 1 only when thr is finite)
+      const uint32_t lo = qp.vals[base], hi = qp.vals[min(base + 1, 2 * HALF - 1)];
+      tbl[e] = make_float2(thr, __builtin_bit_cast(float, lo | (hi << 16)));
+    } else {
+      tbl[e] = make_float2(thr, __builtin_bit_cast(float, base));
+    }
   }
 }
 
@@ -139,6 +144,14 @@ __device__ __forceinline__ uint32_t quantize_one(float tp, const float2* tbl, in
   const int j = med3_i32(floor_neg_to_int(tp), -J, J - 1);
   const float2 e = tbl[j];  // tbl points at bucket 0
   return static_cast<uint32_t>(__builtin_bit_cast(int, e.y)) + (__builtin_fabsf(tp) > e.x ? 1u : 0u);
+}
+
+// The same decision against a table of centroid pairs: the bf16 centroid of the code (low 16 bits)
+__device__ __forceinline__ uint32_t quantize_value(float tp, const float2* tbl, int J) {
+  const int j = med3_i32(floor_neg_to_int(tp), -J, J - 1);
+  const float2 e = tbl[j];
+  const uint32_t vp = __builtin_bit_cast(uint32_t, e.y);
+  return __builtin_fabsf(tp) > e.x ? (vp >> 16) : (vp & 0xFFFFu);
 }
 
 
@@ -217,7 +230,7 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
   uint4 v[kCH];
   load_group(blockIdx.x, v);  // first group in flight during the set-up
 
-  if constexpr (MODE != QuantMode::kRotateOnly) build_table<BITS>(a.qp, tbl_all, tid, blockDim.x);
+  if constexpr (MODE != QuantMode::kRotateOnly) build_table<BITS, MODE == QuantMode::kDecoded>(a.qp, tbl_all, tid, blockDim.x);
   const float2* tbl = tbl_all + J;
 
   // ---- set-up: gather addresses x[perm[j]] (LDS byte offsets) and sign masks of this lane
@@ -423,7 +436,19 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
     } else {
       const float inv_s = lane_sign * a.inv_scale * __builtin_amdgcn_rcpf(s + a.eps);
       const uint32_t off = valid ? lane_row * row_bytes + static_cast<uint32_t>(j0 * BITS / 8) : kDropped;
-      if constexpr (BITS == 4) {
+      if constexpr (MODE == QuantMode::kDecoded) {
+        // bf16 centroids, 16 positions = two groups of 8 in the order 0,2,4,6,1,3,5,7
+        const uint32_t doff = valid ? (lane_row * static_cast<uint32_t>(d) + static_cast<uint32_t>(j0)) * 2u : kDropped;
+#pragma unroll
+        for (int gi = 0; gi < 2; ++gi) {
+          uint32_t v[8];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] = quantize_value(y[8 * gi + i] * inv_s, tbl, J);
+          const v4i_t w = {static_cast<int>(v[0] | (v[2] << 16)), static_cast<int>(v[4] | (v[6] << 16)),
+                           static_cast<int>(v[1] | (v[3] << 16)), static_cast<int>(v[5] | (v[7] << 16))};
+          __builtin_amdgcn_raw_buffer_store_b128(w, codes_rs, doff + 16u * gi, 0, 0);
+        }
+      } else if constexpr (BITS == 4) {
         uint32_t w[2] = {0, 0};
 #pragma unroll
         for (int i = 0; i < kE; ++i) w[i >> 3] |= quantize_one(y[i] * inv_s, tbl, J) << (4 * (i & 7));
@@ -511,12 +536,17 @@ hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, hipSt
 
 template <int H, QuantMode MODE, bool PERM, bool MULTI>
 hipError_t launch_perm(int bits, const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
-  if constexpr (MODE == QuantMode::kRotateOnly) return launch_typed<H, 4, MODE, PERM, MULTI>(a, threads, lds, st);
-  switch (bits) {
-    case 2: return launch_typed<H, 2, MODE, PERM, MULTI>(a, threads, lds, st);
-    case 3: return launch_typed<H, 3, MODE, PERM, MULTI>(a, threads, lds, st);
-    case 4: return launch_typed<H, 4, MODE, PERM, MULTI>(a, threads, lds, st);
-    default: return launch_typed<H, 6, MODE, PERM, MULTI>(a, threads, lds, st);
+  if constexpr (MODE == QuantMode::kRotateOnly) {
+    return launch_typed<H, 4, MODE, PERM, MULTI>(a, threads, lds, st);
+  } else if constexpr (MODE == QuantMode::kDecoded) {
+    return launch_typed<H, 6, MODE, PERM, MULTI>(a, threads, lds, st);
+  } else {
+    switch (bits) {
+      case 2: return launch_typed<H, 2, MODE, PERM, MULTI>(a, threads, lds, st);
+      case 3: return launch_typed<H, 3, MODE, PERM, MULTI>(a, threads, lds, st);
+      case 4: return launch_typed<H, 4, MODE, PERM, MULTI>(a, threads, lds, st);
+      default: return launch_typed<H, 6, MODE, PERM, MULTI>(a, threads, lds, st);
+    }
   }
 }
 
@@ -616,7 +646,8 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
     c.n = rows;
     c.X = X + r0 * ldx;
     c.x_bytes = static_cast<uint32_t>((rows - 1) * ldx * 2 + static_cast<int64_t>(rot.d) * 2);
-    const int64_t cb = static_cast<int64_t>(rot.d) * (mode == QuantMode::kRotateOnly ? 4 : a.qp.bits) / 8;
+    const int out_bits = mode == QuantMode::kRotateOnly ? 4 : mode == QuantMode::kDecoded ? 16 : a.qp.bits;
+    const int64_t cb = static_cast<int64_t>(rot.d) * out_bits / 8;
     if (codes) c.codes = codes + r0 * cb;
     c.codes_bytes = static_cast<uint32_t>(rows * cb);
     const int64_t nb = mode == QuantMode::kWeights ? 2 : 4;
@@ -631,6 +662,10 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
         break;
       case QuantMode::kWeights:
         e = launch_mode<QuantMode::kWeights>(rot.block, bits, c, best_threads, lds, stream);
+        break;
+      case QuantMode::kDecoded:
+        e = bits == 6 ? launch_mode<QuantMode::kDecoded>(rot.block, bits, c, best_threads, lds, stream)
+                      : hipErrorInvalidValue;
         break;
       default:
         e = launch_mode<QuantMode::kRotateOnly>(rot.block, 4, c, best_threads, lds, stream);

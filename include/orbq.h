@@ -182,7 +182,11 @@ int orbq_lut_gemm_act(const uint8_t* x_codes, const float* x_norms, const orbq_c
                       orbq_dtype y_type, int64_t ldy, void* stream);
 
 /* Workspace bytes orbq_linear needs for n tokens of dimension d at bits_a: packed codes
- * (rounded up to 256 bytes) followed by n fp32 norms. */
+ * (rounded up to 256 bytes) followed by n fp32 norms.  For bits_a = 6 the space holds 2 d bytes
+ * per token: with m >= 2048 output columns the layer keeps the codes' bf16 centroids instead of
+ * the packed codes, which its product then stages without decoding (the output is the same
+ * bit for bit; the codes' six-bit lookups cost more than the wider operand once every token row
+ * is decoded for 8 or more column tiles). */
 size_t orbq_linear_workspace_bytes(int64_t n, int64_t d, int32_t bits_a);
 
 /* The online layer: orbq_rpbh_quantize into `workspace`, then orbq_lut_gemm, on one

@@ -102,6 +102,8 @@ def test_sizes():
     assert ws == ((4608 * 1536 + 255) // 256) * 256 + 4608 * 4
     assert lib.orbq_linear_workspace_bytes(10, 3072, 5) == 0
     assert lib.orbq_linear_workspace_bytes(10, 3072, 3) == ((10 * 1152 + 255) // 256) * 256 + 40
+    # 6-bit activations: the layer keeps their bf16 centroids, 2 d bytes per token
+    assert lib.orbq_linear_workspace_bytes(10, 1536, 6) == ((10 * 3072 + 255) // 256) * 256 + 40
 
 
 def test_status_strings():

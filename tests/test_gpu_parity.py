@@ -549,6 +549,47 @@ def test_linear_w3a3_end_to_end(orbq):
     assert e < 2e-3
 
 
+@pytest.mark.parametrize("n,d,h,m,bw,passes,act,out_bf16", [
+    (130, 1536, 128, 2116, 4, 1, "none", False),      # ragged token and weight tiles
+    (777, 320, 64, 2056, 4, 1, "gelu_tanh", True),    # an odd K-tile count (5), GELU epilogue
+    (64, 3072, 128, 2048, 2, 2, "none", True),        # 2-bit weights, two composed RPBH passes
+    (400, 512, 128, 2300, 6, 1, "gelu_erf", False),   # 6-bit weights (their pair table)
+    (1, 1536, 128, 4096, 4, 1, "none", True),         # a single token
+    (300, 1536, 128, 400, 4, 1, "none", False),       # m < 2048: the layer keeps the packed codes
+])
+def test_linear_a6_decoded_equals_codes_path(orbq, n, d, h, m, bw, passes, act, out_bf16):
+    """6-bit activations: with m >= 2048 orbq_linear keeps the codes' bf16 centroids in its
+    workspace and its product stages them without decoding.  Its output equals rpbh_quantize
+    then lut_gemm on the packed codes bit for bit (the same bf16 products summed in the same
+    order), and the first case also matches the oracle chain within 2e-3 of the |dot| scale."""
+    torch = torch_mod()
+    log(f"linear A6 decoded: n={n} d={d} h={h} m={m} W{bw} passes={passes} act={act} bf16={out_bf16}")
+    perm, signs = workloads.rotation_passes(d, passes)
+    rot = orbq.Rotation.create(d, h, perm, signs, passes=passes)
+    cba, ca = gpu_codebook(orbq, d, 6)
+    cbw, cw = gpu_codebook(orbq, d, bw)
+    X = workloads.activations(n, d, seed=1500 + n, kind="heavy", outlier_frac=0.002)
+    W = workloads.weights(m, d, 1501 + m)
+    dX = dev_bf16(X)
+    wc, wn = orbq.fold_weights(dev_bf16(W), rot, cbw)
+    dt = torch.bfloat16 if out_bf16 else torch.float32
+    assert orbq.linear_workspace_bytes(n, d, 6) == -(-n * d * 2 // 256) * 256 + 4 * n
+    Y = orbq.linear(dX, rot, cba, wc, wn, cbw, act=act, out_dtype=dt)
+    xc, xs = orbq.rpbh_quantize(dX, rot, cba)
+    Y2 = orbq.lut_gemm(xc, xs, cba, wc, wn, cbw, d, act=act, out_dtype=dt)
+    torch.cuda.synchronize()
+    assert torch.equal(Y.view(torch.int16) if out_bf16 else Y.view(torch.int32),
+                       Y2.view(torch.int16) if out_bf16 else Y2.view(torch.int32))
+    if n == 130:
+        Pi = oracle.rpbh_composed(d, h, perm, signs, passes)
+        kw, r, _, _ = oracle.fold_weights(workloads.f64_from_bf16_bits(W), Pi, cw)
+        Yo, kx, s = oracle.orbq_linear(workloads.f64_from_bf16_bits(X), Pi, ca, kw, r, cw)
+        den = (np.abs(oracle.decode_lut_bf16(ca)[kx]) @ np.abs(oracle.decode_lut_bf16(cw)[kw]).T) * s[:, None] * r[None, :]
+        e = np.max(np.abs(Y.cpu().numpy() - Yo) / den)
+        log(f"  W{bw}A6 linear vs oracle chain: {e:.3g}")
+        assert e < 2e-3
+
+
 # ----------------------------------------------------------------- edge cases
 def test_edge_cases(orbq):
     torch = torch_mod()
