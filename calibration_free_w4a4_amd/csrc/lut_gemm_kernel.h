@@ -21,8 +21,9 @@
 //   * decode of 4-bit codes: v_perm_b32 byte lookups into the 8 bf16 magnitudes (held in four
 //     registers) plus the sign bit; 2- and 3-bit codes the same into the 4 or 8 signed values;
 //     6-bit codes use a 4096-entry LDS table per code pair.  Activations already decoded to bf16
-//     centroids (the layer's path for 6-bit activations) are staged by direct-to-LDS loads.  Every decoder writes the 8 values of a
-//     16-byte chunk in the order k = 0,2,4,6,1,3,5,7, so A and B agree on k.
+//     centroids (the layer's path for 6-bit activations) are staged by direct-to-LDS loads.
+//     Every decoder writes the 8 values of a 16-byte chunk in the order k = 0,2,4,6,1,3,5,7, so
+//     A and B agree on k.
 //   * LDS: two stages of [BM + BN][64] bf16, 128-byte rows whose 16-byte chunks are xor-swizzled
 //     by (row >> 1) & 7; the MFMA fragment reads (32 rows at one chunk) and the staging stores
 //     (8 rows x 8 chunks per wave) are free of bank conflicts.  One barrier per K tile.
@@ -351,7 +352,7 @@ template <int BA, int BW, bool OUT_BF16, int BM, int BN>
 __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
   using C = Cfg<BM, BN>;
   extern __shared__ __align__(16) unsigned char smem[];
-  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1][2-/6-bit tables]
+  // LDS: [A stage 0][A stage 1][B stage 0][B stage 1][6-bit tables]
   unsigned char* lut = smem + C::LDS;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 3, wn = wave >> 2;
