@@ -493,6 +493,29 @@ def test_linear_a16_weight_only(orbq, n, d, m, bw, out_bf16, passes):
     assert rel < 1.2 * math.sqrt(math.sqrt(3) * math.pi / 2 * 4.0 ** -bw)
 
 
+def test_linear_a16_workspace_reuse(orbq):
+    """The weight-only product keeps rotated tokens and K-split partial sums in the caller's
+    workspace: a workspace filled with 0xFF bytes, reused over calls of different shapes (3
+    chunks of 16 tokens, then 2 tokens, then the first shape again), gives the same outputs as
+    fresh zeroed workspaces, bit for bit (no call depends on what the workspace held)."""
+    torch = torch_mod()
+    d, h = 3072, 128
+    rot = gpu_rotation(orbq, d, h)
+    cb, c = gpu_codebook(orbq, d, 4)
+    W = workloads.weights(1000, d, 911)
+    wc, wn = orbq.fold_weights(dev_bf16(W), rot, cb)
+    need = max(orbq.linear_a16_workspace_bytes(n, d, 1000) for n in (37, 2))
+    ws = torch.full((need,), 0xFF, dtype=torch.uint8, device="cuda")
+    for n in (37, 2, 37):
+        log(f"linear_a16 reused workspace: n={n}")
+        X = dev_bf16(workloads.activations(n, d, seed=912 + n, kind="heavy"))
+        Y = orbq.linear_a16(X, rot, wc, wn, cb, out_dtype=torch.bfloat16, workspace=ws)
+        fresh = torch.zeros((orbq.linear_a16_workspace_bytes(n, d, 1000),), dtype=torch.uint8, device="cuda")
+        Y0 = orbq.linear_a16(X, rot, wc, wn, cb, out_dtype=torch.bfloat16, workspace=fresh)
+        torch.cuda.synchronize()
+        assert torch.equal(Y.view(torch.int16), Y0.view(torch.int16))
+
+
 # ----------------------------------------------------------------- the layer
 def test_linear_equals_quantize_then_gemm(orbq):
     torch = torch_mod()
