@@ -106,3 +106,32 @@ def test_lut_gemm_codes_past_2_31_bytes(orbq, side):
     e = gemm_error(Ysub, Asm, Abg, r_small[ii], r_big[jj])
     log(f"  max relative error {e:.3g}")
     assert e <= 2e-3 + 2.0 ** -8
+
+
+def test_linear_a6_centroids_past_2_31_bytes(orbq):
+    """The layer's path for 6-bit activations keeps the codes' bf16 centroids (2 d bytes per
+    token): 352525 tokens of 3072 make 2.17 GB of them (and of input), so rpbh_quantize and the
+    product both split their launches.  Every repeat of the 1024-token block gives the block's
+    output bit for bit, and the block equals rpbh_quantize then lut_gemm on its packed codes."""
+    torch = torch_mod()
+    d, h, blk, m = 3072, 128, 1024, 2048
+    n = 349525 + 3000
+    reps = -(-n // blk)
+    log(f"linear A6 centroids n={n} d={d} m={m} ({n * d * 2 / 2**30:.2f} GiB of centroids)")
+    perm, signs = workloads.rotation(d)
+    rot = orbq.Rotation.create(d, h, perm, signs)
+    cba, cbw = orbq.Codebook.lloyd_max(d, 6), orbq.Codebook.lloyd_max(d, 4)
+    wc, wn = orbq.fold_weights(dev_bf16(workloads.weights(m, d, 7201)), rot, cbw)
+    B = dev_bf16(workloads.activations(blk, d, seed=7202, kind="heavy"))
+    X = B.repeat(reps, 1)[:n].contiguous()
+    Y = orbq.linear(X, rot, cba, wc, wn, cbw, out_dtype=torch.bfloat16)
+    del X
+    torch.cuda.synchronize()
+    first = Y[:blk]
+    for r in range(1, reps):
+        rows = min(blk, n - r * blk)
+        assert torch.equal(Y[r * blk:r * blk + rows], first[:rows]), f"repeat {r} differs"
+    xc, xs = orbq.rpbh_quantize(B, rot, cba)
+    Y2 = orbq.lut_gemm(xc, xs, cba, wc, wn, cbw, d, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(first.view(torch.int16), Y2.view(torch.int16))
