@@ -8,13 +8,13 @@ namespace {
 // ============================================================================ A16 (weight-only)
 // Y[t][j] = r'_j sum_k bf16(x'_tk) bf16(C_w[w_jk]) for a few tokens (t < 16 per launch):
 // x' = Pi x in fp32 (the rotate-only pass of rpbh_quantize), codes streamed from HBM once.
-// Workgroup = 4 waves; each wave owns 64 weight rows (four 16-row MFMA column blocks) and one
-// split of the K range; v_mfma_f32_16x16x32_bf16 with the tokens as the M side (rows past the
-// token count read as zero).  A super-step covers 128 codes: lane (m = l % 16, g = l / 16)
+// A workgroup owns 64 weight rows (four 16-row MFMA column blocks); each of its waves takes one
+// split of the K range, with v_mfma_f32_16x16x32_bf16 and the tokens as the M side (rows past
+// the token count read as zero).  A super-step covers 128 codes: lane (m = l % 16, g = l / 16)
 // holds codes 32 g .. 32 g + 31 of it, i.e. one 16-byte (4-bit) load per row block, and takes
 // them 8 at a time in four MFMAs.  The k order inside each 8 (0,2,4,6,1,3,5,7, the decoders'
-// order) is applied to x' as well.  Partial sums of each split go to a workspace; a second
-// kernel adds the splits and applies r'.
+// order) is applied to x' as well.  The waves' partial sums meet in LDS, where they are added
+// in split order and scaled by r'.
 // A buffer resource from wave-uniform values, forced into scalar registers: the compiler keeps
 // values derived from 64-bit compares and selects in VGPRs, which would wrap every load that
 // uses the resource in a waterfall loop.
@@ -26,17 +26,19 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
                                            __builtin_amdgcn_readfirstlane(bytes), kBufWord3);
 }
 
-constexpr int kA16Waves = 4;
-constexpr int kA16Rows = 64;                  // weight rows per wave
+constexpr int kA16MaxSplits = 16;            // waves per workgroup, one K split each
+constexpr int kA16MaxCB = 4;                  // 16-row MFMA column blocks per workgroup (2 or 4)
 constexpr int kA16SS = 128;                   // codes per super-step
 
 struct A16Args {
   const float* xr;       // x' [nt][d] fp32
   const uint8_t* wc;
-  float* part;           // [splits][nt][m]
+  const uint16_t* wn;    // r' bf16 [m]
+  void* Y;
+  int64_t ldy;
   int64_t m;
   int32_t d, nt, rb;     // rb = code bytes per weight row
-  int32_t ss_per_split, nss, row_blocks;
+  int32_t ss_per_split, nss, splits;
   uint32_t xr_bytes;     // nt * d * 4
   uint32_t lt_lo, lt_hi, ht_lo, ht_hi;
   uint16_t mag[32];
@@ -104,23 +106,24 @@ struct CodesA16<6> {
   }
 };
 
-template <int BW>
-__global__ __launch_bounds__(64 * kA16Waves) void k_a16_partial(A16Args a) {
+template <int BW, bool OUT_BF16, int CB>
+__global__ __launch_bounds__(64 * kA16MaxSplits) void k_a16(A16Args a) {
+  constexpr int kA16Rows = 16 * CB;  // weight rows of this workgroup
   __shared__ __align__(16) unsigned char lut[BW == 6 ? 4096 * 4 : 16];
   __shared__ uint16_t mags[32];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  extern __shared__ float red[];  // [splits][nt][64] partial sums
+  const int tid = threadIdx.x, lane = tid & 63, split = tid >> 6, nthreads = blockDim.x;
   if constexpr (needs_lut(BW)) {
     if (tid < 32) mags[tid] = a.mag[tid];
     __syncthreads();
-    build_lut<BW, 64 * kA16Waves>(mags, lut, tid);
+    build_lut<BW>(mags, lut, tid, nthreads);
     __syncthreads();
   }
   const Tab4 tw{a.lt_lo, a.lt_hi, a.ht_lo, a.ht_hi};
-  const int rblk = blockIdx.x % a.row_blocks, split = blockIdx.x / a.row_blocks;
   const int ss0 = split * a.ss_per_split;
   const int ss1 = min(a.nss, ss0 + a.ss_per_split);
   const int m16 = lane & 15, g = lane >> 4;
-  const int64_t row_base = (static_cast<int64_t>(rblk) * kA16Waves + wave) * kA16Rows;
+  const int64_t row_base = static_cast<int64_t>(blockIdx.x) * kA16Rows;
 
   // x' rows past nt read as zero; code rows past m read as zero (never stored)
   const __amdgpu_buffer_rsrc_t xs = uniform_rsrc(a.xr, a.xr_bytes);
@@ -128,9 +131,9 @@ __global__ __launch_bounds__(64 * kA16Waves) void k_a16_partial(A16Args a) {
   const uint32_t wc_bytes = rows_left <= 0 ? 0u : static_cast<uint32_t>(min<int64_t>(rows_left, kA16Rows) * a.rb);
   const __amdgpu_buffer_rsrc_t ws = uniform_rsrc(a.wc + (rows_left > 0 ? row_base * a.rb : 0), wc_bytes);
   const uint32_t xoff = static_cast<uint32_t>(m16 < a.nt ? m16 * a.d * 4 : 0x7FFFFFF0) ;
-  f32x4_t acc[4];
+  f32x4_t acc[CB];
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) acc[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
+  for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int ss = ss0; ss < ss1; ++ss) {
     const int k0 = ss * kA16SS + 32 * g;
@@ -145,9 +148,9 @@ __global__ __launch_bounds__(64 * kA16Waves) void k_a16_partial(A16Args a) {
       xv[4 * c + 2] = __builtin_bit_cast(float, v.z);
       xv[4 * c + 3] = __builtin_bit_cast(float, v.w);
     }
-    CodesA16<BW> cw[4];
+    CodesA16<BW> cw[CB];
 #pragma unroll
-    for (int cb = 0; cb < 4; ++cb)
+    for (int cb = 0; cb < CB; ++cb)
       cw[cb].load(ws, static_cast<uint32_t>((16 * cb + m16) * a.rb + k0 * BW / 8));
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -156,36 +159,30 @@ __global__ __launch_bounds__(64 * kA16Waves) void k_a16_partial(A16Args a) {
                            static_cast<__bf16>(x8[6]), static_cast<__bf16>(x8[1]), static_cast<__bf16>(x8[3]),
                            static_cast<__bf16>(x8[5]), static_cast<__bf16>(x8[7])};
 #pragma unroll
-      for (int cb = 0; cb < 4; ++cb) {
+      for (int cb = 0; cb < CB; ++cb) {
         const uint4 bw = cw[cb].get(s, tw, lut);
         acc[cb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, __builtin_bit_cast(bf16x8_t, bw), acc[cb], 0, 0, 0);
       }
     }
   }
   // D[t][n]: t = 4 (lane / 16) + i, n = lane % 16 of column block cb
-  float* part = a.part + static_cast<int64_t>(split) * a.nt * a.m;
 #pragma unroll
-  for (int cb = 0; cb < 4; ++cb) {
-    const int64_t row = row_base + 16 * cb + m16;
+  for (int cb = 0; cb < CB; ++cb)
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int t = 4 * g + i;
-      if (t < a.nt && row < a.m) part[static_cast<int64_t>(t) * a.m + row] = acc[cb][i];
+      if (t < a.nt) red[(split * a.nt + t) * kA16Rows + 16 * cb + m16] = acc[cb][i];
     }
-  }
-}
-
-template <bool OUT_BF16>
-__global__ __launch_bounds__(256) void k_a16_reduce(const float* part, int splits, int nt, int64_t m,
-                                                    const uint16_t* wn, void* Y, int64_t ldy) {
-  const int64_t total = static_cast<int64_t>(nt) * m;
-  for (int64_t e = blockIdx.x * 256ll + threadIdx.x; e < total; e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t t = e / m, j = e - t * m;
-    float acc = 0.0f;
-    for (int s = 0; s < splits; ++s) acc += part[(static_cast<int64_t>(s) * nt + t) * m + j];
-    const float v = acc * __builtin_bit_cast(float, static_cast<uint32_t>(wn[j]) << 16);
-    if constexpr (OUT_BF16) reinterpret_cast<__bf16*>(Y)[t * ldy + j] = static_cast<__bf16>(v);
-    else reinterpret_cast<float*>(Y)[t * ldy + j] = v;
+  __syncthreads();
+  for (int e = tid; e < a.nt * kA16Rows; e += nthreads) {
+    const int t = e / kA16Rows, rr = e - t * kA16Rows;
+    const int64_t j = row_base + rr;
+    if (j >= a.m) continue;
+    float sum = 0.0f;
+    for (int sp = 0; sp < a.splits; ++sp) sum += red[(sp * a.nt + t) * kA16Rows + rr];
+    const float v = sum * __builtin_bit_cast(float, static_cast<uint32_t>(a.wn[j]) << 16);
+    if constexpr (OUT_BF16) reinterpret_cast<__bf16*>(a.Y)[t * a.ldy + j] = static_cast<__bf16>(v);
+    else reinterpret_cast<float*>(a.Y)[t * a.ldy + j] = v;
   }
 }
 
@@ -194,52 +191,83 @@ __global__ __launch_bounds__(256) void k_a16_reduce(const float* part, int split
 
 using namespace lg;
 
-// Splits of the K range for the weight-only product: enough workgroups to stream the codes
-// from every compute unit (about 1024), each split a whole number of 128-code super-steps.
-void a16_splits(int64_t m, int64_t d, int* splits, int* ss_per_split, int* row_blocks) {
-  const int64_t rb = (m + kA16Waves * kA16Rows - 1) / (kA16Waves * kA16Rows);
+// Splits of the K range for the weight-only product: up to 16, one wave each, every split a
+// whole number of 128-code super-steps; a workgroup holds 64 weight rows and all their splits.
+void a16_splits(int64_t d, int* splits, int* ss_per_split) {
   const int nss = static_cast<int>(d / kA16SS);
-  const int64_t want = std::max<int64_t>(1, std::min<int64_t>(nss, (1024 + rb - 1) / rb));
-  const int per = static_cast<int>((nss + want - 1) / want);
+  const int per = (nss + kA16MaxSplits - 1) / kA16MaxSplits;
   *ss_per_split = per;
   *splits = (nss + per - 1) / per;
-  *row_blocks = static_cast<int>(rb);
 }
 
+namespace {
+
+// 16-row column blocks per workgroup, 4 or 2: the fewest rows on the busiest compute unit when
+// the workgroups are dealt out; 4 blocks share each wave's x' loads among more MFMAs and win
+// ties.  (One block per workgroup balances finer but loads x' once per 4 MFMAs: at the AdaLN
+// shape, 2 x 3072 -> 18432, a call took 17.9 us with it against 15.4 with 2 and 15.8 with 4.)
+int a16_column_blocks(int64_t m) {
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+    cus = 256;
+  int best = kA16MaxCB;
+  int64_t best_rows = INT64_MAX;
+  for (int cb = kA16MaxCB; cb >= 2; cb /= 2) {
+    const int64_t wg = (m + 16 * cb - 1) / (16 * cb);
+    const int64_t rows = (wg + cus - 1) / cus * 16 * cb;
+    if (rows < best_rows) {
+      best_rows = rows;
+      best = cb;
+    }
+  }
+  return best;
+}
+
+template <int CB>
+void launch_k_a16(int bits, bool out_bf16, dim3 grid, dim3 blk, size_t red, hipStream_t st, const A16Args& a) {
+  if (out_bf16) {
+    switch (bits) {
+      case 2: hipLaunchKernelGGL((k_a16<2, true, CB>), grid, blk, red, st, a); break;
+      case 3: hipLaunchKernelGGL((k_a16<3, true, CB>), grid, blk, red, st, a); break;
+      case 4: hipLaunchKernelGGL((k_a16<4, true, CB>), grid, blk, red, st, a); break;
+      default: hipLaunchKernelGGL((k_a16<6, true, CB>), grid, blk, red, st, a); break;
+    }
+  } else {
+    switch (bits) {
+      case 2: hipLaunchKernelGGL((k_a16<2, false, CB>), grid, blk, red, st, a); break;
+      case 3: hipLaunchKernelGGL((k_a16<3, false, CB>), grid, blk, red, st, a); break;
+      case 4: hipLaunchKernelGGL((k_a16<4, false, CB>), grid, blk, red, st, a); break;
+      default: hipLaunchKernelGGL((k_a16<6, false, CB>), grid, blk, red, st, a); break;
+    }
+  }
+}
+
+}  // namespace
+
 int launch_a16_gemm(const float* x_rot, int nt, int64_t d, const uint8_t* w_codes, const uint16_t* w_norms,
-                    const DecodeParams& dw, int64_t m, float* part, void* Y, int y_bf16, int64_t ldy,
-                    hipStream_t stream) {
+                    const DecodeParams& dw, int64_t m, void* Y, int y_bf16, int64_t ldy, hipStream_t stream) {
   A16Args a{};
   a.xr = x_rot;
   a.wc = w_codes;
-  a.part = part;
+  a.wn = w_norms;
+  a.Y = Y;
+  a.ldy = ldy;
   a.m = m;
   a.d = static_cast<int32_t>(d);
   a.nt = nt;
   a.rb = static_cast<int32_t>(d * dw.bits / 8);
   a.nss = static_cast<int32_t>(d / kA16SS);
-  int splits = 1;
-  a16_splits(m, d, &splits, &a.ss_per_split, &a.row_blocks);
+  a16_splits(d, &a.splits, &a.ss_per_split);
   a.xr_bytes = static_cast<uint32_t>(static_cast<int64_t>(nt) * d * 4);
   tab4(dw, &a.lt_lo, &a.lt_hi, &a.ht_lo, &a.ht_hi);
   for (int i = 0; i < 32; ++i) a.mag[i] = dw.mag[i];
-  const int grid = a.row_blocks * splits;
-  switch (dw.bits) {
-    case 2: hipLaunchKernelGGL(k_a16_partial<2>, dim3(grid), dim3(64 * kA16Waves), 0, stream, a); break;
-    case 3: hipLaunchKernelGGL(k_a16_partial<3>, dim3(grid), dim3(64 * kA16Waves), 0, stream, a); break;
-    case 4: hipLaunchKernelGGL(k_a16_partial<4>, dim3(grid), dim3(64 * kA16Waves), 0, stream, a); break;
-    default: hipLaunchKernelGGL(k_a16_partial<6>, dim3(grid), dim3(64 * kA16Waves), 0, stream, a); break;
-  }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return static_cast<int>(e);
-  const int64_t total = static_cast<int64_t>(nt) * m;
-  const int rgrid = static_cast<int>(std::min<int64_t>((total + 255) / 256, 4096));
-  if (y_bf16)
-    hipLaunchKernelGGL(k_a16_reduce<true>, dim3(rgrid), dim3(256), 0, stream, part, splits, nt, m, w_norms, Y, ldy);
-  else
-    hipLaunchKernelGGL(k_a16_reduce<false>, dim3(rgrid), dim3(256), 0, stream, part, splits, nt, m, w_norms, Y, ldy);
+  const int cb = a16_column_blocks(m);
+  const dim3 grid(static_cast<unsigned>((m + 16 * cb - 1) / (16 * cb))), blk(64 * a.splits);
+  const size_t red = static_cast<size_t>(a.splits) * nt * 16 * cb * sizeof(float);
+  if (cb == 2) launch_k_a16<2>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a);
+  else launch_k_a16<4>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a);
   return static_cast<int>(hipGetLastError());
 }
-
 
 }  // namespace orbq

@@ -312,12 +312,10 @@ constexpr int64_t kA16Tokens = 16;  // tokens per weight-only launch
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-size_t a16_ws_bytes(int64_t n, int64_t d, int64_t m) {
+// [x' fp32 nt x d][norms fp32 nt]: the rotated tokens of one 16-token chunk (m does not enter)
+size_t a16_ws_bytes(int64_t n, int64_t d, int64_t /*m*/) {
   const int64_t nt = std::min<int64_t>(n, kA16Tokens);
-  int splits = 1, per = 1, rb = 1;
-  orbq::a16_splits(m, d, &splits, &per, &rb);
-  return round256(static_cast<size_t>(nt * d * 4)) + round256(static_cast<size_t>(nt * 4)) +
-         static_cast<size_t>(splits) * static_cast<size_t>(nt) * static_cast<size_t>(m) * 4;
+  return round256(static_cast<size_t>(nt * d * 4)) + round256(static_cast<size_t>(nt * 4));
 }
 
 }  // namespace
@@ -353,7 +351,6 @@ ORBQ_API int orbq_linear_a16(const void* X, int64_t n, int64_t d, int64_t ldx, c
   const int64_t nt_max = std::min<int64_t>(n, kA16Tokens);
   float* xr = static_cast<float*>(workspace);
   float* norms = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + round256(static_cast<size_t>(nt_max * d * 4)));
-  float* part = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(norms) + round256(static_cast<size_t>(nt_max * 4)));
   orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs, rot->passes < 1 ? 1 : rot->passes};
   const int64_t esz = y_type == ORBQ_BF16 ? 2 : 4;
   const hipStream_t st = static_cast<hipStream_t>(stream);
@@ -362,7 +359,7 @@ ORBQ_API int orbq_linear_a16(const void* X, int64_t n, int64_t d, int64_t ldx, c
     int e = orbq::launch_rpbh_quantize(orbq::QuantMode::kRotateOnly, static_cast<const uint16_t*>(X) + t0 * ldx, nt,
                                        ldx, ra, nullptr, 0.0f, nullptr, norms, xr, st);
     if (e == hipSuccess)
-      e = orbq::launch_a16_gemm(xr, nt, d, w_codes, static_cast<const uint16_t*>(w_norms), dw, m, part,
+      e = orbq::launch_a16_gemm(xr, nt, d, w_codes, static_cast<const uint16_t*>(w_norms), dw, m,
                                 static_cast<unsigned char*>(Y) + t0 * ldy * esz, y_type == ORBQ_BF16, ldy, st);
     if (e != hipSuccess) return hip_status(e, what);
   }

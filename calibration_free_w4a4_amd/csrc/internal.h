@@ -65,11 +65,10 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
                          hipStream_t stream);
 
 // Weight-only product (bf16 activations, rotated in fp32): K-range splits and launcher.
-// x_rot [nt][d] fp32 with nt <= 16; part [splits][nt][m] fp32 workspace; d % 128 == 0.
-void a16_splits(int64_t m, int64_t d, int* splits, int* ss_per_split, int* row_blocks);
+// x_rot [nt][d] fp32 with nt <= 16; d % 128 == 0.
+void a16_splits(int64_t d, int* splits, int* ss_per_split);
 int launch_a16_gemm(const float* x_rot, int nt, int64_t d, const uint8_t* w_codes, const uint16_t* w_norms,
-                    const DecodeParams& dw, int64_t m, float* part, void* Y, int y_bf16, int64_t ldy,
-                    hipStream_t stream);
+                    const DecodeParams& dw, int64_t m, void* Y, int y_bf16, int64_t ldy, hipStream_t stream);
 
 int launch_flatness(const uint16_t* X, int64_t n, int32_t d, int64_t ldx, float* rho3, float* rhoinf,
                     hipStream_t stream);

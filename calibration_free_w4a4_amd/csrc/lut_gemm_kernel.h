@@ -213,11 +213,11 @@ __device__ __forceinline__ uint16_t mag_signed(const uint16_t* mag, uint32_t cod
 constexpr int lut_bytes_dev(int bits) { return bits == 6 ? 4096 * 4 : 0; }
 constexpr bool needs_lut(int bits) { return bits == 6; }
 
-template <int BITS, int NT = kThreads>
-__device__ __forceinline__ void build_lut(const uint16_t* mag, unsigned char* p, int tid) {
+template <int BITS>
+__device__ __forceinline__ void build_lut(const uint16_t* mag, unsigned char* p, int tid, int nthreads = kThreads) {
   if constexpr (BITS == 6) {
     uint32_t* l = reinterpret_cast<uint32_t*>(p);
-    for (int i = tid; i < 4096; i += NT)
+    for (int i = tid; i < 4096; i += nthreads)
       l[i] = mag_signed(mag, i & 63, 6) | (static_cast<uint32_t>(mag_signed(mag, i >> 6, 6)) << 16);
   }
 }
