@@ -7,13 +7,14 @@ namespace {
 
 // ============================================================================ A16 (weight-only)
 // Y[t][j] = r'_j sum_k bf16(x'_tk) bf16(C_w[w_jk]) for a few tokens (t < 16 per launch):
-// x' = Pi x in fp32 (the rotate-only pass of rpbh_quantize), codes streamed from HBM once.
+// x' = Pi x computed in fp32 and stored as bf16 by the rotate pass of rpbh_quantize, in the
+// decoders' k order, so that 16 bytes of a row are one MFMA operand; codes streamed from HBM once.
 // A workgroup owns 64 weight rows (four 16-row MFMA column blocks); each of its waves takes one
 // split of the K range, with v_mfma_f32_16x16x32_bf16 and the tokens as the M side (rows past
 // the token count read as zero).  A super-step covers 128 codes: lane (m = l % 16, g = l / 16)
 // holds codes 32 g .. 32 g + 31 of it, i.e. one 16-byte (4-bit) load per row block, and takes
-// them 8 at a time in four MFMAs.  The k order inside each 8 (0,2,4,6,1,3,5,7, the decoders'
-// order) is applied to x' as well.  The waves' partial sums meet in LDS, where they are added
+// them 8 at a time in four MFMAs, each with the matching 16 bytes of x' (already in the
+// decoders' k order 0,2,4,6,1,3,5,7 within each 8).  The waves' partial sums meet in LDS, where they are added
 // in split order and scaled by r'.
 // A buffer resource from wave-uniform values, forced into scalar registers: the compiler keeps
 // values derived from 64-bit compares and selects in VGPRs, which would wrap every load that
@@ -31,7 +32,7 @@ constexpr int kA16MaxCB = 4;                  // 16-row MFMA column blocks per w
 constexpr int kA16SS = 128;                   // codes per super-step
 
 struct A16Args {
-  const float* xr;       // x' [nt][d] fp32
+  const uint16_t* xr;    // x' [nt][d] bf16, k order 0,2,4,6,1,3,5,7 within each 8
   const uint8_t* wc;
   const uint16_t* wn;    // r' bf16 [m]
   void* Y;
@@ -39,7 +40,7 @@ struct A16Args {
   int64_t m;
   int32_t d, nt, rb;     // rb = code bytes per weight row
   int32_t ss_per_split, nss, splits;
-  uint32_t xr_bytes;     // nt * d * 4
+  uint32_t xr_bytes;     // nt * d * 2
   uint32_t lt_lo, lt_hi, ht_lo, ht_hi;
   uint16_t mag[32];
 };
@@ -130,34 +131,26 @@ __global__ __launch_bounds__(64 * kA16MaxSplits) void k_a16(A16Args a) {
   const int64_t rows_left = a.m - row_base;
   const uint32_t wc_bytes = rows_left <= 0 ? 0u : static_cast<uint32_t>(min<int64_t>(rows_left, kA16Rows) * a.rb);
   const __amdgpu_buffer_rsrc_t ws = uniform_rsrc(a.wc + (rows_left > 0 ? row_base * a.rb : 0), wc_bytes);
-  const uint32_t xoff = static_cast<uint32_t>(m16 < a.nt ? m16 * a.d * 4 : 0x7FFFFFF0) ;
+  const uint32_t xoff = static_cast<uint32_t>(m16 < a.nt ? m16 * a.d * 2 : 0x7FFFFFF0);
   f32x4_t acc[CB];
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
   for (int ss = ss0; ss < ss1; ++ss) {
     const int k0 = ss * kA16SS + 32 * g;
-    // A: 32 consecutive x' values of token m16
-    float xv[32];
+    // A: the 32 x' values of token m16 that match the lane's codes, as four MFMA operands
+    bf16x8_t xv[4];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-      const uint4 v = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-          xs, xoff + static_cast<uint32_t>((k0 + 4 * c) * 4), 0, 0));
-      xv[4 * c] = __builtin_bit_cast(float, v.x);
-      xv[4 * c + 1] = __builtin_bit_cast(float, v.y);
-      xv[4 * c + 2] = __builtin_bit_cast(float, v.z);
-      xv[4 * c + 3] = __builtin_bit_cast(float, v.w);
-    }
+    for (int c = 0; c < 4; ++c)
+      xv[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+          xs, xoff + static_cast<uint32_t>((k0 + 8 * c) * 2), 0, 0));
     CodesA16<BW> cw[CB];
 #pragma unroll
     for (int cb = 0; cb < CB; ++cb)
       cw[cb].load(ws, static_cast<uint32_t>((16 * cb + m16) * a.rb + k0 * BW / 8));
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      const float* x8 = xv + 8 * s;
-      const bf16x8_t av = {static_cast<__bf16>(x8[0]), static_cast<__bf16>(x8[2]), static_cast<__bf16>(x8[4]),
-                           static_cast<__bf16>(x8[6]), static_cast<__bf16>(x8[1]), static_cast<__bf16>(x8[3]),
-                           static_cast<__bf16>(x8[5]), static_cast<__bf16>(x8[7])};
+      const bf16x8_t av = xv[s];
 #pragma unroll
       for (int cb = 0; cb < CB; ++cb) {
         const uint4 bw = cw[cb].get(s, tw, lut);
@@ -245,7 +238,7 @@ void launch_k_a16(int bits, bool out_bf16, dim3 grid, dim3 blk, size_t red, hipS
 
 }  // namespace
 
-int launch_a16_gemm(const float* x_rot, int nt, int64_t d, const uint8_t* w_codes, const uint16_t* w_norms,
+int launch_a16_gemm(const uint16_t* x_rot, int nt, int64_t d, const uint8_t* w_codes, const uint16_t* w_norms,
                     const DecodeParams& dw, int64_t m, void* Y, int y_bf16, int64_t ldy, hipStream_t stream) {
   A16Args a{};
   a.xr = x_rot;
@@ -259,7 +252,7 @@ int launch_a16_gemm(const float* x_rot, int nt, int64_t d, const uint8_t* w_code
   a.rb = static_cast<int32_t>(d * dw.bits / 8);
   a.nss = static_cast<int32_t>(d / kA16SS);
   a16_splits(d, &a.splits, &a.ss_per_split);
-  a.xr_bytes = static_cast<uint32_t>(static_cast<int64_t>(nt) * d * 4);
+  a.xr_bytes = static_cast<uint32_t>(static_cast<int64_t>(nt) * d * 2);
   tab4(dw, &a.lt_lo, &a.lt_hi, &a.ht_lo, &a.ht_hi);
   for (int i = 0; i < 32; ++i) a.mag[i] = dw.mag[i];
   const int cb = a16_column_blocks(m);

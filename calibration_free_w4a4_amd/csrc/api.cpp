@@ -312,10 +312,10 @@ constexpr int64_t kA16Tokens = 16;  // tokens per weight-only launch
 
 size_t round256(size_t x) { return (x + 255) & ~size_t(255); }
 
-// [x' fp32 nt x d][norms fp32 nt]: the rotated tokens of one 16-token chunk (m does not enter)
+// [x' bf16 nt x d][norms fp32 nt]: the rotated tokens of one 16-token chunk (m does not enter)
 size_t a16_ws_bytes(int64_t n, int64_t d, int64_t /*m*/) {
   const int64_t nt = std::min<int64_t>(n, kA16Tokens);
-  return round256(static_cast<size_t>(nt * d * 4)) + round256(static_cast<size_t>(nt * 4));
+  return round256(static_cast<size_t>(nt * d * 2)) + round256(static_cast<size_t>(nt * 4));
 }
 
 }  // namespace
@@ -349,15 +349,15 @@ ORBQ_API int orbq_linear_a16(const void* X, int64_t n, int64_t d, int64_t ldx, c
   orbq::DecodeParams dw;
   orbq::build_decode_params(cb_w->centroids, cb_w->bits, &dw);
   const int64_t nt_max = std::min<int64_t>(n, kA16Tokens);
-  float* xr = static_cast<float*>(workspace);
-  float* norms = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + round256(static_cast<size_t>(nt_max * d * 4)));
+  uint16_t* xr = static_cast<uint16_t*>(workspace);
+  float* norms = reinterpret_cast<float*>(static_cast<unsigned char*>(workspace) + round256(static_cast<size_t>(nt_max * d * 2)));
   orbq::RotArgs ra{rot->d, rot->block, rot->perm, rot->signs, rot->passes < 1 ? 1 : rot->passes};
   const int64_t esz = y_type == ORBQ_BF16 ? 2 : 4;
   const hipStream_t st = static_cast<hipStream_t>(stream);
   for (int64_t t0 = 0; t0 < n; t0 += kA16Tokens) {
     const int nt = static_cast<int>(std::min<int64_t>(kA16Tokens, n - t0));
-    int e = orbq::launch_rpbh_quantize(orbq::QuantMode::kRotateOnly, static_cast<const uint16_t*>(X) + t0 * ldx, nt,
-                                       ldx, ra, nullptr, 0.0f, nullptr, norms, xr, st);
+    int e = orbq::launch_rpbh_quantize(orbq::QuantMode::kRotateBf16, static_cast<const uint16_t*>(X) + t0 * ldx, nt,
+                                       ldx, ra, nullptr, 0.0f, nullptr, norms, reinterpret_cast<float*>(xr), st);
     if (e == hipSuccess)
       e = orbq::launch_a16_gemm(xr, nt, d, w_codes, static_cast<const uint16_t*>(w_norms), dw, m,
                                 static_cast<unsigned char*>(Y) + t0 * ldy * esz, y_type == ORBQ_BF16, ldy, st);

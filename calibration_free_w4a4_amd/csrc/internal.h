@@ -58,16 +58,18 @@ struct RotArgs {
 // kDecoded: activations written as the bf16 centroids of their codes (qp.vals), [n][d] bf16 with
 // the 8 values of each aligned group of 8 positions in the order 0,2,4,6,1,3,5,7 (the order in
 // which the product stages its operands), for a product that stages them without decoding.
-enum class QuantMode { kActivations, kWeights, kRotateOnly, kDecoded };
+// kRotateBf16: the rotated rows x' = Pi x (no quantization) as bf16, rounded to nearest even,
+// in the same order within each group of 8 positions, for the weight-only product.
+enum class QuantMode { kActivations, kWeights, kRotateOnly, kDecoded, kRotateBf16 };
 
 int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t ldx, const RotArgs& rot,
                          const QuantParams* qp, float eps, uint8_t* codes, void* norms, float* x_rot,
                          hipStream_t stream);
 
 // Weight-only product (bf16 activations, rotated in fp32): K-range splits and launcher.
-// x_rot [nt][d] fp32 with nt <= 16; d % 128 == 0.
+// x_rot [nt][d] bf16 (QuantMode::kRotateBf16) with nt <= 16; d % 128 == 0.
 void a16_splits(int64_t d, int* splits, int* ss_per_split);
-int launch_a16_gemm(const float* x_rot, int nt, int64_t d, const uint8_t* w_codes, const uint16_t* w_norms,
+int launch_a16_gemm(const uint16_t* x_rot, int nt, int64_t d, const uint8_t* w_codes, const uint16_t* w_norms,
                     const DecodeParams& dw, int64_t m, void* Y, int y_bf16, int64_t ldy, hipStream_t stream);
 
 int launch_flatness(const uint16_t* X, int64_t n, int32_t d, int64_t ldx, float* rho3, float* rhoinf,

@@ -230,7 +230,8 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
   uint4 v[kCH];
   load_group(blockIdx.x, v);  // first group in flight during the set-up
 
-  if constexpr (MODE != QuantMode::kRotateOnly) build_table<BITS, MODE == QuantMode::kDecoded>(a.qp, tbl_all, tid, blockDim.x);
+  constexpr bool kRotate = MODE == QuantMode::kRotateOnly || MODE == QuantMode::kRotateBf16;
+  if constexpr (!kRotate) build_table<BITS, MODE == QuantMode::kDecoded>(a.qp, tbl_all, tid, blockDim.x);
   const float2* tbl = tbl_all + J;
 
   // ---- set-up: gather addresses x[perm[j]] (LDS byte offsets) and sign masks of this lane
@@ -433,6 +434,22 @@ __global__ __launch_bounds__(1024) void k_rpbh_quantize(QuantKernelArgs a) {
       }
       __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, s), norms_rs,
                                             (valid && q == 0) ? lane_row * 4u : kDropped, 0, 0);
+    } else if constexpr (MODE == QuantMode::kRotateBf16) {
+      // bf16 (nearest even), 16 positions = two groups of 8 in the order 0,2,4,6,1,3,5,7
+      const float sc = a.inv_scale * lane_sign;
+      const uint32_t off = valid ? (lane_row * static_cast<uint32_t>(d) + j0) * 2u : kDropped;
+#pragma unroll
+      for (int gi = 0; gi < 2; ++gi) {
+        const float* v = y + 8 * gi;
+        auto pair = [&](int lo, int hi) {
+          const bf16x2_t p = {static_cast<__bf16>(v[lo] * sc), static_cast<__bf16>(v[hi] * sc)};
+          return __builtin_bit_cast(int, p);
+        };
+        const v4i_t w = {pair(0, 2), pair(4, 6), pair(1, 3), pair(5, 7)};
+        __builtin_amdgcn_raw_buffer_store_b128(w, rot_rs, off + 16u * gi, 0, 0);
+      }
+      __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(int, s), norms_rs,
+                                            (valid && q == 0) ? lane_row * 4u : kDropped, 0, 0);
     } else {
       const float inv_s = lane_sign * a.inv_scale * __builtin_amdgcn_rcpf(s + a.eps);
       const uint32_t off = valid ? lane_row * row_bytes + static_cast<uint32_t>(j0 * BITS / 8) : kDropped;
@@ -536,7 +553,7 @@ hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, hipSt
 
 template <int H, QuantMode MODE, bool PERM, bool MULTI>
 hipError_t launch_perm(int bits, const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
-  if constexpr (MODE == QuantMode::kRotateOnly) {
+  if constexpr (MODE == QuantMode::kRotateOnly || MODE == QuantMode::kRotateBf16) {
     return launch_typed<H, 4, MODE, PERM, MULTI>(a, threads, lds, st);
   } else if constexpr (MODE == QuantMode::kDecoded) {
     return launch_typed<H, 6, MODE, PERM, MULTI>(a, threads, lds, st);
@@ -625,7 +642,8 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
   a.seg = seg;
   a.nseg = a.lpt / seg;
   const float rsqrt_h = 1.0f / __builtin_sqrtf(static_cast<float>(rot.block));
-  a.inv_scale = (mode == QuantMode::kRotateOnly) ? rsqrt_h : static_cast<float>(static_cast<double>(a.qp.scale) /
+  const bool rotate = mode == QuantMode::kRotateOnly || mode == QuantMode::kRotateBf16;
+  a.inv_scale = rotate ? rsqrt_h : static_cast<float>(static_cast<double>(a.qp.scale) /
                                                                                  std::sqrt(static_cast<double>(rot.block)));
   size_t lds = ((static_cast<size_t>(a.tg) * rot.d * 2 + 15) & ~size_t(15)) +
                sizeof(float2) * 2 * a.qp.J + sizeof(float) * a.tg * a.nseg;
@@ -653,8 +671,9 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
     const int64_t nb = mode == QuantMode::kWeights ? 2 : 4;
     c.norms = static_cast<unsigned char*>(norms) + r0 * nb;
     c.norms_bytes = static_cast<uint32_t>(rows * nb);
-    if (x_rot) c.x_rot = x_rot + r0 * rot.d;
-    c.rot_bytes = x_rot ? static_cast<uint32_t>(rows * rot.d * 4) : 0u;
+    const int64_t rot_esz = mode == QuantMode::kRotateBf16 ? 2 : 4;  // bytes per rotated coordinate
+    if (x_rot) c.x_rot = reinterpret_cast<float*>(reinterpret_cast<unsigned char*>(x_rot) + r0 * rot.d * rot_esz);
+    c.rot_bytes = x_rot ? static_cast<uint32_t>(rows * rot.d * rot_esz) : 0u;
     c.ngroups = static_cast<int>((rows + a.tg - 1) / a.tg);
     switch (mode) {
       case QuantMode::kActivations:
@@ -662,6 +681,9 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
         break;
       case QuantMode::kWeights:
         e = launch_mode<QuantMode::kWeights>(rot.block, bits, c, best_threads, lds, stream);
+        break;
+      case QuantMode::kRotateBf16:
+        e = launch_mode<QuantMode::kRotateBf16>(rot.block, 4, c, best_threads, lds, stream);
         break;
       case QuantMode::kDecoded:
         e = bits == 6 ? launch_mode<QuantMode::kDecoded>(rot.block, bits, c, best_threads, lds, stream)

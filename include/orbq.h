@@ -216,7 +216,7 @@ int orbq_linear_act(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq
  *   rot      rotation the weights were folded with (any passes)
  *   w_codes, w_norms, cb_w, m   as for orbq_lut_gemm
  *   workspace [device] >= orbq_linear_a16_workspace_bytes(n, d, m), 256-byte aligned: the
- *            rotated tokens of a 16-token chunk (fp32) and their norms
+ *            rotated tokens of a 16-token chunk (bf16) and their norms
  *   Y        [device] float or bf16 [n][ldy], ldy >= m
  * Errors as orbq_linear; d % 128 != 0 gives ORBQ_ERR_UNSUPPORTED. */
 size_t orbq_linear_a16_workspace_bytes(int64_t n, int64_t d, int64_t m);
