@@ -608,20 +608,26 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
     }
     return;
   }
-  // edge tile: per-element bounds checks
+  // edge tile: per-element bounds checks.  The 16 row scales of a 32-row block are loaded
+  // first, together (row index clamped), so that their latencies overlap instead of following
+  // one another behind the bounds checks.
   int64_t cols[C::TJ];
 #pragma unroll
   for (int j = 0; j < C::TJ; ++j) {
     cols[j] = col0 + wn * C::TN + 32 * j + l32;
-    rn[j] = cols[j] < a.m ? __builtin_bit_cast(float, static_cast<uint32_t>(a.wn[cols[j]]) << 16) : 0.0f;
+    rn[j] = __builtin_bit_cast(float, static_cast<uint32_t>(a.wn[min(cols[j], a.m - 1)]) << 16);
   }
 #pragma unroll
   for (int i = 0; i < C::TI; ++i) {
+    float srow[16];
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      srow[r] = a.xs[min(row0 + wm * C::TM + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3), a.n - 1)];
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int64_t row = row0 + wm * C::TM + 32 * i + 8 * (r >> 2) + 4 * g + (r & 3);
       if (row >= a.n) continue;
-      const float sr = a.xs[row];
+      const float sr = srow[r];
       if constexpr (OUT_BF16) {
         __bf16* yrow = reinterpret_cast<__bf16*>(a.Y) + row * a.ldy;
 #pragma unroll
@@ -660,11 +666,14 @@ inline hipError_t launch_bw(int cfg, bool out_bf16, const GemmArgs& a, int grid,
 
 template <int BA>
 inline hipError_t launch_ba(int bw, int cfg, bool out_bf16, const GemmArgs& a, int grid, size_t lds, hipStream_t st) {
-  if constexpr (BA == 3) return launch_bw<3, 3>(cfg, out_bf16, a, grid, lds, st);  // 3-bit pairs only with 3-bit
-  switch (bw) {
-    case 2: return launch_bw<BA, 2>(cfg, out_bf16, a, grid, lds, st);
-    case 4: return launch_bw<BA, 4>(cfg, out_bf16, a, grid, lds, st);
-    default: return launch_bw<BA, 6>(cfg, out_bf16, a, grid, lds, st);
+  if constexpr (BA == 3) {
+    return launch_bw<3, 3>(cfg, out_bf16, a, grid, lds, st);  // 3-bit pairs only with 3-bit
+  } else {
+    switch (bw) {
+      case 2: return launch_bw<BA, 2>(cfg, out_bf16, a, grid, lds, st);
+      case 4: return launch_bw<BA, 4>(cfg, out_bf16, a, grid, lds, st);
+      default: return launch_bw<BA, 6>(cfg, out_bf16, a, grid, lds, st);
+    }
   }
 }
 
