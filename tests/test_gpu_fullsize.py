@@ -105,7 +105,7 @@ def test_headline_every_element(orbq):
 
 
 @pytest.mark.parametrize("name", ["flux_qkv", "flux_mlp_up", "flux_mlp_down", "flux_mlp_up_w2a4",
-                                  "wan_ffn_up", "wan_ffn_down"])
+                                  "flux_mlp_up_w3a3", "wan_ffn_up", "wan_ffn_down"])
 def test_layer_full_size_sampled(orbq, name):
     L = workloads.CONFIGS[name]
     log(f"full size {name}: n={L.n} d={L.d} m={L.m} W{L.bits_w}A{L.bits_a}")

@@ -167,6 +167,8 @@ CONFIGS: dict[str, Layer] = {
     # W2A4 variant of the MLP-up shape, outlier fraction 0.5%
     "flux_mlp_up_w2a4": Layer("flux_mlp_up_w2a4", 4608, 3072, 12288, 2, 4, 128, "heavy", 401, 402,
                               0.005, 30.0),
+    # W3A3 variant of the headline layer (same tokens and weights, 8-centroid codebooks)
+    "flux_mlp_up_w3a3": Layer("flux_mlp_up_w3a3", 4608, 3072, 12288, 3, 3, 128, "heavy", 301, 302),
     # Wan 2.1 1.3B video FFN, W4A6 (21 frames x 30 x 52 latent tokens)
     "wan_ffn_up": Layer("wan_ffn_up", 32760, 1536, 8960, 4, 6, 128, "video", 501, 502),
     "wan_ffn_down": Layer("wan_ffn_down", 32760, 8960, 1536, 4, 6, 128, "gelu", 504, 503),
