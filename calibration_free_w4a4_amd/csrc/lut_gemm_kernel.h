@@ -581,13 +581,24 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
       rn[j] = __builtin_bit_cast(float, static_cast<uint32_t>(a.wn[col0 + col]) << 16);
       voff[j] = static_cast<uint32_t>(((wm * C::TM + 4 * g) * ldy + col) * esz);
     }
+    // the row scales of the next 32-row block are loaded before the current block's stores, so
+    // that waiting for them never waits for stores (one counter covers both on gfx9)
+    typedef float f32x2_t __attribute__((ext_vector_type(2)));
+    const float* xsw = a.xs + row0 + wm * C::TM + 4 * g;
+    f32x2_t sv[2][8];
+    auto load_s = [&](int i, f32x2_t (&dst)[8]) {
+#pragma unroll
+      for (int r = 0; r < 16; r += 2)
+        dst[r >> 1] = *reinterpret_cast<const f32x2_t*>(xsw + 32 * i + 8 * (r >> 2) + (r & 3));
+    };
+    load_s(0, sv[0]);
 #pragma unroll
     for (int i = 0; i < C::TI; ++i) {
+      if (i + 1 < C::TI) load_s(i + 1, sv[(i + 1) & 1]);
 #pragma unroll
       for (int r = 0; r < 16; r += 2) {
         const int rr0 = 32 * i + 8 * (r >> 2) + (r & 3);  // row within the wave band (less 4 g)
-        const int64_t row = row0 + wm * C::TM + rr0 + 4 * g;
-        const float s0 = a.xs[row], s1 = a.xs[row + 1];
+        const float s0 = sv[i & 1][r >> 1].x, s1 = sv[i & 1][r >> 1].y;
         const int so0 = static_cast<int>(rr0 * ldy * esz), so1 = static_cast<int>((rr0 + 1) * ldy * esz);
 #pragma unroll
         for (int j = 0; j < C::TJ; ++j) {
