@@ -41,8 +41,9 @@
  *
  * Memory: every buffer is owned by the caller.  Pointers marked [device] are HIP device
  * pointers, [host] are host pointers.  The library allocates no device memory: the
- * workspaces of orbq_linear, orbq_linear_act and orbq_linear_a16 come from the caller.  Calls are asynchronous on `stream`
- * (a hipStream_t; NULL = the default stream) and re-entrant; argument errors are
+ * workspaces of orbq_linear, orbq_linear_act and orbq_linear_a16 come from the caller.
+ * Calls are asynchronous on `stream` (a hipStream_t; NULL = the default stream) and
+ * re-entrant (calls that share a workspace must not overlap); argument errors are
  * detected on the host before anything is launched and are returned synchronously.
  * Device faults surface at the caller's next synchronisation.  Device arrays (perm,
  * signs) are read, never validated, by the kernels: a perm entry outside [0, d) is
