@@ -192,6 +192,8 @@ def codes_row_bytes(d: int, bits: int) -> int:
 
 
 def linear_workspace_bytes(n: int, d: int, bits_a: int) -> int:
+    """Bytes of orbq_linear's workspace: the token codes and norms (for 6-bit activations,
+    room for the codes' bf16 centroids, which the layer keeps when m >= 2048)."""
     return int(load().orbq_linear_workspace_bytes(n, d, bits_a))
 
 
@@ -286,6 +288,8 @@ def linear(X, rot: Rotation, cb_a: Codebook, w_codes, w_norms, cb_w: Codebook, e
 
 
 def linear_a16_workspace_bytes(n: int, d: int, m: int) -> int:
+    """Bytes of orbq_linear_a16's workspace: one 16-token chunk of rotated bf16 tokens and
+    their norms."""
     return int(load().orbq_linear_a16_workspace_bytes(n, d, m))
 
 
