@@ -56,6 +56,11 @@ constexpr int KT = 64;          // K tile (codes)
 constexpr int kRow = KT * 2;    // bytes of one staged bf16 row
 constexpr int kThreads = 512;
 constexpr uint32_t kBufWord3 = 0x00020000u;  // raw (untyped) buffer resource, gfx9 family
+// Cache policy of the full-tile Y stores: sc0 sc1, system-scope coherence.  Each Y line goes
+// through L2 to memory (the memory-side Infinity Cache, where the next layer finds it) as it is
+// written, instead of waiting dirty in L2 until a later access evicts it; no Y line is read again
+// by this kernel.  Measured 0.6-0.9 % faster per step than the default policy on one box.
+constexpr int kYStorePolicy = 1 | 16;
 
 template <int BM_, int BN_>
 struct Cfg {
@@ -608,11 +613,11 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
             typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
             const bf16x2_t p = {static_cast<__bf16>(v0), static_cast<__bf16>(v1)};
             const uint32_t u = __builtin_bit_cast(uint32_t, p);
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(u), ys, voff[j], so0, 0);
-            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(u >> 16), ys, voff[j], so1, 0);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(u), ys, voff[j], so0, kYStorePolicy);
+            __builtin_amdgcn_raw_buffer_store_b16(static_cast<unsigned short>(u >> 16), ys, voff[j], so1, kYStorePolicy);
           } else {
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v0), ys, voff[j], so0, 0);
-            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v1), ys, voff[j], so1, 0);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v0), ys, voff[j], so0, kYStorePolicy);
+            __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(uint32_t, v1), ys, voff[j], so1, kYStorePolicy);
           }
         }
       }
