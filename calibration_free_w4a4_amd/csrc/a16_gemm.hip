@@ -1,4 +1,6 @@
 // a16_gemm: the weight-only product with bf16 activations (W{2,3,4,6}A16).
+#include <algorithm>
+
 #include "lut_gemm_kernel.h"
 
 namespace orbq {
@@ -9,7 +11,7 @@ namespace {
 // Y[t][j] = r'_j sum_k bf16(x'_tk) bf16(C_w[w_jk]) for a few tokens (t < 16 per launch):
 // x' = Pi x computed in fp32 and stored as bf16 by the rotate pass of rpbh_quantize, in the
 // decoders' k order, so that 16 bytes of a row are one MFMA operand; codes streamed from HBM once.
-// A workgroup owns 64 weight rows (four 16-row MFMA column blocks); each of its waves takes one
+// A workgroup owns 16 CB weight rows (CB 16-row MFMA column blocks, 2 to 5); each of its waves takes one
 // split of the K range, with v_mfma_f32_16x16x32_bf16 and the tokens as the M side (rows past
 // the token count read as zero).  A super-step covers 128 codes: lane (m = l % 16, g = l / 16)
 // holds codes 32 g .. 32 g + 31 of it, i.e. one 16-byte (4-bit) load per row block, and takes
@@ -28,7 +30,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t uniform_rsrc(const void* base,
 }
 
 constexpr int kA16MaxSplits = 16;            // waves per workgroup, one K split each
-constexpr int kA16MaxCB = 4;                  // 16-row MFMA column blocks per workgroup (2 or 4)
+constexpr int kA16MaxCB = 5;                  // 16-row MFMA column blocks per workgroup (2 to 5)
 constexpr int kA16SS = 128;                   // codes per super-step
 
 struct A16Args {
@@ -112,7 +114,7 @@ __global__ __launch_bounds__(64 * kA16MaxSplits) void k_a16(A16Args a) {
   constexpr int kA16Rows = 16 * CB;  // weight rows of this workgroup
   __shared__ __align__(16) unsigned char lut[BW == 6 ? 4096 * 4 : 16];
   __shared__ uint16_t mags[32];
-  extern __shared__ float red[];  // [splits][nt][64] partial sums
+  extern __shared__ float red[];  // [splits][nt][16 CB] partial sums
   const int tid = threadIdx.x, lane = tid & 63, split = tid >> 6, nthreads = blockDim.x;
   if constexpr (needs_lut(BW)) {
     if (tid < 32) mags[tid] = a.mag[tid];
@@ -185,7 +187,7 @@ __global__ __launch_bounds__(64 * kA16MaxSplits) void k_a16(A16Args a) {
 using namespace lg;
 
 // Splits of the K range for the weight-only product: up to 16, one wave each, every split a
-// whole number of 128-code super-steps; a workgroup holds 64 weight rows and all their splits.
+// whole number of 128-code super-steps; a workgroup holds its weight rows and all their splits.
 void a16_splits(int64_t d, int* splits, int* ss_per_split) {
   const int nss = static_cast<int>(d / kA16SS);
   const int per = (nss + kA16MaxSplits - 1) / kA16MaxSplits;
@@ -195,18 +197,26 @@ void a16_splits(int64_t d, int* splits, int* ss_per_split) {
 
 namespace {
 
-// 16-row column blocks per workgroup, 4 or 2: the fewest rows on the busiest compute unit when
-// the workgroups are dealt out; 4 blocks share each wave's x' loads among more MFMAs and win
-// ties.  (One block per workgroup balances finer but loads x' once per 4 MFMAs: at the AdaLN
-// shape, 2 x 3072 -> 18432, a call took 17.9 us with it against 15.4 with 2 and 15.8 with 4.)
-int a16_column_blocks(int64_t m) {
+// 16-row column blocks per workgroup, 2 to 5.  The smallest count whose workgroups fit one per
+// compute unit: each workgroup then has its compute unit to itself, and a wave's x' loads serve
+// as many MFMAs as that allows.  The partial sums [splits][nt][16 CB] floats must fit the 64 KB
+// of dynamic LDS.  When no count fits one workgroup per compute unit (m > 80 per CU), the count
+// of 4 or 2 that puts the fewest rows on the busiest compute unit, 4 on ties.  Measured on 256
+// compute units (same outputs bit for bit for every count): 16 x 3072 -> 18432 took 14.2 us with
+// 5 blocks (231 workgroups) against 16.4, 18.1 and 18.8 with 3, 4 and 2; 2 x 3072 -> 18432
+// 3-4 % less with 5 than with 2; 16 x 3072 -> 12288 13.6 with 3 (256 workgroups), 13.5 with 4.
+int a16_column_blocks(int64_t m, int nt, int splits) {
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
     cus = 256;
-  int best = kA16MaxCB;
+  const int lds_cap = static_cast<int>(65536 / (static_cast<int64_t>(splits) * nt * 16 * sizeof(float)));
+  const int top = std::min(kA16MaxCB, lds_cap);
+  for (int cb = 2; cb <= top; ++cb)
+    if ((m + 16 * cb - 1) / (16 * cb) <= cus) return cb;
+  int best = 4;
   int64_t best_rows = INT64_MAX;
-  for (int cb = kA16MaxCB; cb >= 2; cb /= 2) {
+  for (int cb = 4; cb >= 2; cb /= 2) {
     const int64_t wg = (m + 16 * cb - 1) / (16 * cb);
     const int64_t rows = (wg + cus - 1) / cus * 16 * cb;
     if (rows < best_rows) {
@@ -255,11 +265,15 @@ int launch_a16_gemm(const uint16_t* x_rot, int nt, int64_t d, const uint8_t* w_c
   a.xr_bytes = static_cast<uint32_t>(static_cast<int64_t>(nt) * d * 2);
   tab4(dw, &a.lt_lo, &a.lt_hi, &a.ht_lo, &a.ht_hi);
   for (int i = 0; i < 32; ++i) a.mag[i] = dw.mag[i];
-  const int cb = a16_column_blocks(m);
+  const int cb = a16_column_blocks(m, nt, a.splits);
   const dim3 grid(static_cast<unsigned>((m + 16 * cb - 1) / (16 * cb))), blk(64 * a.splits);
   const size_t red = static_cast<size_t>(a.splits) * nt * 16 * cb * sizeof(float);
-  if (cb == 2) launch_k_a16<2>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a);
-  else launch_k_a16<4>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a);
+  switch (cb) {
+    case 2: launch_k_a16<2>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a); break;
+    case 3: launch_k_a16<3>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a); break;
+    case 4: launch_k_a16<4>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a); break;
+    default: launch_k_a16<5>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a); break;
+  }
   return static_cast<int>(hipGetLastError());
 }
 

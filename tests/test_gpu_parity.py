@@ -456,12 +456,14 @@ def test_lut_gemm_act_none_and_linear_act(orbq):
     (2, 3072, 18432, 4, False, 1), (1, 256, 100, 4, False, 1), (3, 3072, 777, 3, True, 1),
     (1, 12288, 3072, 4, False, 1), (5, 3072, 1000, 6, True, 1), (16, 1536, 1000, 6, True, 1),
     (37, 3072, 700, 2, False, 1), (5, 12288, 3072, 4, True, 1), (2, 3072, 600, 4, False, 2),
-    (2, 3072, 16384, 4, True, 1), (3, 3072, 24576, 4, False, 1)])
+    (2, 3072, 16384, 4, True, 1), (3, 3072, 24576, 4, False, 1), (16, 3072, 12288, 4, True, 1),
+    (16, 3072, 18432, 4, False, 1)])
 def test_linear_a16_weight_only(orbq, n, d, m, bw, out_bf16, passes):
     """orbq_linear_a16 (bf16 activations rotated, weight codes decoded) against the oracle's
     weight-only product: 16-token chunks, a composed rotation, ragged m, 2/3/4/6-bit weights, the
-    AdaLN modulation shape (2 x 3072 -> 18432), and workgroups of 32 and 64 weight rows
-    (m = 18432 or 24576, and 16384, on 256 compute units)."""
+    AdaLN modulation shape (2 x 3072 -> 18432), and workgroups of 2 to 5 16-row column blocks
+    (on 256 compute units: m = 24576 takes 2, 12288 with 16 tokens 3, 16384 4, 18432 5, the last
+    also with 16 tokens and the largest partial-sum buffer, 60 KB of LDS)."""
     torch = torch_mod()
     log(f"linear_a16 n={n} d={d} m={m} W{bw} bf16={out_bf16} passes={passes}")
     h = 64 if d == 256 else 128
