@@ -174,9 +174,15 @@ class Codebook:
         return cls(d, bits, c)
 
     def struct(self) -> _Codebook:
-        c = np.ascontiguousarray(self.centroids, dtype=np.float32)
+        c = self.centroids
+        cached = getattr(self, "_struct", None)
+        if cached is not None and self._keep is c and (cached.d, cached.bits) == (self.d, self.bits):
+            return cached  # the struct points at the live float32 array itself
+        c = np.ascontiguousarray(c, dtype=np.float32)
         self._keep = c
-        return _Codebook(self.d, self.bits, c.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+        st = _Codebook(self.d, self.bits, c.ctypes.data_as(ctypes.POINTER(ctypes.c_float)))
+        self._struct = st if c is self.centroids else None
+        return st
 
 
 @functools.lru_cache(maxsize=None)

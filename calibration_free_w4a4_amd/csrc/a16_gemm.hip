@@ -206,10 +206,7 @@ namespace {
 // 5 blocks (231 workgroups) against 16.4, 18.1 and 18.8 with 3, 4 and 2; 2 x 3072 -> 18432
 // 3-4 % less with 5 than with 2; 16 x 3072 -> 12288 13.6 with 3 (256 workgroups), 13.5 with 4.
 int a16_column_blocks(int64_t m, int nt, int splits) {
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-    cus = 256;
+  const int cus = device_cus();
   const int lds_cap = static_cast<int>(65536 / (static_cast<int64_t>(splits) * nt * 16 * sizeof(float)));
   const int top = std::min(kA16MaxCB, lds_cap);
   for (int cb = 2; cb <= top; ++cb)

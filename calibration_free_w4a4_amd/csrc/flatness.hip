@@ -63,8 +63,7 @@ __global__ __launch_bounds__(64 * kWaves) void k_flatness(const uint16_t* X, int
 
 int launch_flatness(const uint16_t* X, int64_t n, int32_t d, int64_t ldx, float* rho3, float* rhoinf,
                     hipStream_t stream) {
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  const int cus = device_cus();
   const int64_t want = (n + kWaves - 1) / kWaves;
   const int grid = static_cast<int>(std::max<int64_t>(1, std::min<int64_t>(want, static_cast<int64_t>(cus) * 8)));
   hipLaunchKernelGGL(k_flatness, dim3(grid), dim3(64 * kWaves), 0, stream, X, n, d, ldx, rho3, rhoinf);

@@ -66,6 +66,10 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
                          const QuantParams* qp, float eps, uint8_t* codes, void* norms, float* x_rot,
                          hipStream_t stream);
 
+// The current device's compute-unit count (256 if the runtime cannot say), cached per device
+// and host thread.
+int device_cus();
+
 // Weight-only product (bf16 activations, rotated in fp32): K-range splits and launcher.
 // x_rot [nt][d] bf16 (QuantMode::kRotateBf16) with nt <= 16; d % 128 == 0.
 void a16_splits(int64_t d, int* splits, int* ss_per_split);

@@ -8,6 +8,11 @@ namespace {
 
 size_t lut_bytes(int bits) { return bits == 6 ? 4096 * 4 : 0; }
 
+}  // namespace
+}  // namespace lg
+
+using namespace lg;
+
 int device_cus() {
   static thread_local int cached_dev = -1, cached_cus = 0;
   int dev = 0;
@@ -20,11 +25,6 @@ int device_cus() {
   }
   return cached_cus;
 }
-
-}  // namespace
-}  // namespace lg
-
-using namespace lg;
 
 int launch_lut_gemm(const uint8_t* x_codes, const float* x_norms, const DecodeParams& da, const uint8_t* w_codes,
                     const uint16_t* w_norms, const DecodeParams& dw, int64_t n, int64_t m, int64_t d, void* Y,
