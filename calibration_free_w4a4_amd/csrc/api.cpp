@@ -74,7 +74,10 @@ int check_dim(int64_t d, const char* what) {
 
 int quant_params(const orbq_codebook* cb, orbq::QuantParams* qp, const char* what) {
   if (orbq::build_quant_params(cb->centroids, cb->bits, qp))
-    return fail(ORBQ_ERR_CODEBOOK, "%s: no power-of-two scale separates the decision thresholds", what);
+    return fail(ORBQ_ERR_CODEBOOK,
+                "%s: no power-of-two scale 2^k separates the decision thresholds (at most one per unit of t * 2^k; "
+                "2^k <= 1024 for codes of 4 bits or fewer)",
+                what);
   return ORBQ_OK;
 }
 

@@ -210,7 +210,7 @@ int build_quant_params(const float* c, int bits, QuantParams* qp) {
     }
     const double top = nb ? static_cast<double>(qp->thr_gt[nb - 1]) : 0.0;
     const int J = static_cast<int>(std::floor(top)) + 2;
-    if (!ok || J > kMaxTableHalf) continue;
+    if (!ok || J > kMaxTableHalf || (bits <= 4 && sc > kMaxFullScale)) continue;
     qp->scale = static_cast<float>(sc);
     qp->J = J;
     return 0;

@@ -9,6 +9,10 @@ namespace orbq {
 
 constexpr int kMaxPosBoundaries = 31;  // 6-bit codebooks: N/2 - 1 positive decision boundaries
 constexpr int kMaxTableHalf = 256;     // quantizer table holds buckets -J..J-1, J <= 256
+// 2-, 3- and 4-bit codebooks: the quantize kernel's table covers every bucket of t' in
+// [-2^k, 2^k] (2^(k+1) + 4 entries of 8 bytes), so 2^k is capped at 1024 (16 KB of LDS).  Every
+// Lloyd-Max codebook of f_d up to d = 16384 needs 2^k <= 1024.
+constexpr int kMaxFullScale = 1024;
 
 // Decision thresholds of one codebook in the scaled coordinate t' = t * 2^k.
 //

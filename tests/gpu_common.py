@@ -69,3 +69,22 @@ def gemm_error(Y_gpu: np.ndarray, A: np.ndarray, B: np.ndarray, s: np.ndarray, r
     Y = (A @ B.T) * s[:, None] * r[None, :]
     den = (np.abs(A) @ np.abs(B).T) * s[:, None] * r[None, :]
     return float(np.max(np.abs(Y_gpu - Y) / np.maximum(den, 1e-300)))
+
+
+def check_rprime(got: np.ndarray, s_ref: np.ndarray, what: str) -> int:
+    """Stored weight-row norms r' (bf16, as float64) against the oracle's exact norms s_ref: equal
+    to the oracle's round-to-nearest-even bf16, or one bf16 ulp away only where the exact norm
+    lies within 1e-6 (relative) of the bf16 rounding midpoint between the two (the fp32 norm the
+    kernel rounds carries ~1e-7 relative error).  Returns the count of such midpoint cases."""
+    r_ref = oracle.bf16_rne(s_ref)
+    diff = got != r_ref
+    n = int(diff.sum())
+    if n:
+        ulp = 2.0 ** (np.floor(np.log2(r_ref[diff])) - 7)
+        assert np.all(np.abs(got[diff] - r_ref[diff]) <= ulp), f"{what}: r' more than one bf16 ulp off"
+        mid = r_ref[diff] + np.sign(got[diff] - r_ref[diff]) * ulp / 2
+        far = np.abs(s_ref[diff] - mid) > 1e-6 * s_ref[diff]
+        assert not far.any(), (f"{what}: r' one ulp off away from a rounding midpoint "
+                               f"(norm {s_ref[diff][far][:3]}, got {got[diff][far][:3]})")
+    log(f"  {what}: r' differs from the oracle's bf16 at {n} midpoint rows of {got.size}")
+    return n

@@ -17,7 +17,7 @@ import pytest
 import oracle
 import workloads
 from tests.conftest import oracle_codebook
-from tests.gpu_common import check_codes, dense_pi, dev_bf16, gemm_error, log, torch_mod
+from tests.gpu_common import check_codes, check_rprime, dense_pi, dev_bf16, gemm_error, log, torch_mod
 
 pytestmark = pytest.mark.gpu
 
@@ -74,9 +74,7 @@ def _check_rows(name, src_bits, codes, norms, idx, L, bits, weights):
     k_ref, s_ref, T_ref = oracle.quantize_activations(workloads.f64_from_bf16_bits(src_bits[idx]), Pi, c)
     check_codes(oracle.unpack_codes(codes[idx], bits, L.d), k_ref, T_ref, c, name)
     if weights:
-        r_ref = oracle.bf16_rne(s_ref)
-        ulp = 2.0 ** (np.floor(np.log2(r_ref)) - 7)
-        assert np.all(np.abs(norms[idx] - r_ref) <= ulp), f"{name}: r' more than one bf16 ulp off"
+        check_rprime(norms[idx], s_ref, f"{name} r'")
     else:
         assert np.max(np.abs(norms[idx] - s_ref) / s_ref) < 1e-6, f"{name}: s off"
 
@@ -120,3 +118,100 @@ def test_layer_full_size_sampled(orbq, name):
     i2 = _sample(L.n, None, 256, 13)
     j2 = _sample(L.m, None, 256, 14)
     _check_gemm("Y (second sampled block)", L, xc, xs, wc, wn, Y, i2, j2)
+
+
+@pytest.mark.parametrize("act", ["gelu_tanh", "gelu_erf"])
+def test_flux_mlp_pair_chain(orbq, act):
+    """The FLUX MLP pair (9216 tokens, 3072 -> 12288 -> 3072, W4A4, block 128) chained as a model
+    runs it: the up layer through orbq_linear_act with GELU in the epilogue and bf16 output, and
+    that exact bf16 hidden tensor fed to the down layer (rpbh_quantize on d = 12288, then
+    lut_gemm to bf16).  Checked against the oracle on sampled rows:
+      * the hidden tensor: the oracle's float64 GELU of the product of the up layer's own codes;
+      * the down layer's token codes and s: the oracle's quantizer on the identical bf16 tensor;
+      * the down layer's weight codes and r';
+      * the down layer's outputs from identical codes."""
+    torch = torch_mod()
+    Lu, Ld = workloads.CONFIGS["flux_mlp_up"], workloads.CONFIGS["flux_mlp_down"]
+    n = Lu.n
+    log(f"MLP pair {act}: {n} x {Lu.d} -> {Lu.m} -> {Ld.m}")
+    X, Wu = workloads.layer_inputs(Lu)
+    Wd = workloads.weights(Ld.m, Ld.d, Ld.w_seed)
+    rot_u = orbq.Rotation.create(Lu.d, Lu.block, *workloads.rotation(Lu.d))
+    rot_d = orbq.Rotation.create(Ld.d, Ld.block, *workloads.rotation(Ld.d))
+    cb_u, cb_d = orbq.Codebook.lloyd_max(Lu.d, 4), orbq.Codebook.lloyd_max(Ld.d, 4)
+    dX = dev_bf16(X)
+    wcu, wnu = orbq.fold_weights(dev_bf16(Wu), rot_u, cb_u)
+    wcd, wnd = orbq.fold_weights(dev_bf16(Wd), rot_d, cb_d)
+    H = torch.empty((n, Lu.m), dtype=torch.bfloat16, device="cuda")
+    orbq.linear(dX, rot_u, cb_u, wcu, wnu, cb_u, out=H, act=act)
+    xcu, xsu = orbq.rpbh_quantize(dX, rot_u, cb_u)  # the up layer's token codes, for the check
+    xcd = torch.empty((n, orbq.codes_row_bytes(Ld.d, 4)), dtype=torch.uint8, device="cuda")
+    xsd = torch.empty((n,), dtype=torch.float32, device="cuda")
+    orbq.rpbh_quantize(H, rot_d, cb_d, out_codes=xcd, out_norms=xsd)
+    Y = torch.empty((n, Ld.m), dtype=torch.bfloat16, device="cuda")
+    orbq.lut_gemm(xcd, xsd, cb_d, wcd, wnd, cb_d, Ld.d, out=Y)
+    torch.cuda.synchronize()
+    ii = _sample(n, X, 24, 21)
+    jj = _sample(Lu.m, None, 64, 22)
+    # hidden tensor on sampled rows and columns
+    Hs = H[torch.from_numpy(ii).cuda()].float().cpu().numpy().astype(np.float64)
+    xcu_h, xsu_h = xcu.cpu().numpy(), xsu.cpu().numpy().astype(np.float64)
+    wcu_h, wnu_h = wcu.cpu().numpy(), wnu.float().cpu().numpy().astype(np.float64)
+    cu = oracle_codebook(Lu.d, 4)
+    ku_x, ku_w = oracle.unpack_codes(xcu_h[ii], 4, Lu.d), oracle.unpack_codes(wcu_h[jj], 4, Lu.d)
+    Gref = oracle.lut_gemm_act(ku_x, xsu_h[ii], cu, ku_w, wnu_h[jj], cu, act)
+    lut = oracle.decode_lut_bf16(cu)
+    den = (np.abs(lut[ku_x]) @ np.abs(lut[ku_w]).T) * xsu_h[ii][:, None] * wnu_h[jj][None, :]
+    e = float(np.max(np.abs(Hs[:, jj] - Gref) / den))
+    log(f"  hidden {act}(Y_up): {len(ii)} x {len(jj)} outputs, error / |dot| scale {e:.3g}")
+    assert e <= 2.0 ** -8 + 1e-5
+    assert np.isfinite(Hs).all()
+    # the down layer on the identical bf16 hidden tensor
+    H_bits = Hs.astype(np.float32).view(np.uint32) >> 16  # bf16 values are exact in fp32
+    H_bits = H_bits.astype(np.uint16)
+    xcd_h, xsd_h = xcd.cpu().numpy(), xsd.cpu().numpy().astype(np.float64)
+    cd = oracle_codebook(Ld.d, 4)
+    Pi = dense_pi(Ld.d, Ld.block)
+    k_ref, s_ref, T_ref = oracle.quantize_activations(workloads.f64_from_bf16_bits(H_bits), Pi, cd)
+    check_codes(oracle.unpack_codes(xcd_h[ii], 4, Ld.d), k_ref, T_ref, cd, "down token codes (sampled rows)")
+    assert np.max(np.abs(xsd_h[ii] - s_ref) / s_ref) < 1e-6, "down s off"
+    wcd_h, wnd_h = wcd.cpu().numpy(), wnd.float().cpu().numpy().astype(np.float64)
+    jd = _sample(Ld.m, None, 24, 23)
+    _check_rows("down weight codes (sampled rows)", Wd, wcd_h, wnd_h, jd, Ld, 4, True)
+    Yh = Y.float().cpu().numpy()
+    _check_gemm("down Y (sampled block)", Ld, xcd_h, xsd_h, wcd_h, wnd_h, Yh, ii, _sample(Ld.m, None, 256, 24))
+    _check_gemm("down Y (second sample)", Ld, xcd_h, xsd_h, wcd_h, wnd_h, Yh, _sample(n, None, 256, 25),
+                _sample(Ld.m, None, 256, 26))
+
+
+@pytest.mark.parametrize("bits,weights", [(2, False), (3, False), (4, False), (4, True)])
+def test_quantize_full_range_table(orbq, bits, weights):
+    """rpbh_quantize / fold_weights where every workgroup runs many token groups (4200 rows of
+    d = 12288), the launch that fills the full-range decision table (no clamp of the bucket
+    index): sampled rows' codes and norms against the oracle, and the poisoned-output check
+    (every byte of every row written)."""
+    torch = torch_mod()
+    d, h, n = 12288, 128, 4200
+    log(f"full-range table: d={d} n={n} bits={bits} weights={weights}")
+    src = workloads.weights(n, d, 811) if weights else workloads.activations(n, d, 812 + bits, kind="heavy")
+    rot = orbq.Rotation.create(d, h, *workloads.rotation(d))
+    cb = orbq.Codebook.lloyd_max(d, bits)
+    c = oracle_codebook(d, bits)
+    dsrc = dev_bf16(src)
+    rb = orbq.codes_row_bytes(d, bits)
+    codes = torch.full((n, rb), 0xFF, dtype=torch.uint8, device="cuda")
+    norms = torch.full((n,), -1.0, dtype=torch.bfloat16 if weights else torch.float32, device="cuda")
+    (orbq.fold_weights if weights else orbq.rpbh_quantize)(dsrc, rot, cb, out_codes=codes, out_norms=norms)
+    codes0 = torch.zeros_like(codes)
+    norms0 = torch.zeros_like(norms)
+    (orbq.fold_weights if weights else orbq.rpbh_quantize)(dsrc, rot, cb, out_codes=codes0, out_norms=norms0)
+    torch.cuda.synchronize()
+    assert torch.equal(codes, codes0) and torch.equal(norms.view(torch.uint8), norms0.view(torch.uint8))
+    idx = _sample(n, None if weights else src, 20, 31)
+    k_ref, s_ref, T_ref = oracle.quantize_activations(workloads.f64_from_bf16_bits(src[idx]), dense_pi(d, h), c)
+    check_codes(oracle.unpack_codes(codes.cpu().numpy()[idx], bits, d), k_ref, T_ref, c, f"{bits}-bit codes")
+    got = norms.float().cpu().numpy().astype(np.float64)[idx]
+    if weights:
+        check_rprime(got, s_ref, "r'")
+    else:
+        assert np.max(np.abs(got - s_ref) / s_ref) < 1e-6

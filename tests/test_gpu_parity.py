@@ -16,7 +16,8 @@ import pytest
 import oracle
 import workloads
 from tests.conftest import oracle_codebook
-from tests.gpu_common import (check_codes, dense_pi, dev_bf16, gemm_error, host_bits, log, torch_mod)
+from tests.gpu_common import (check_codes, check_rprime, dense_pi, dev_bf16, gemm_error, host_bits, log,
+                              torch_mod)
 
 pytestmark = pytest.mark.gpu
 
@@ -124,8 +125,7 @@ def test_quantize_large_blocks_and_identity(orbq, h, ident, weights):
     check_codes(oracle.unpack_codes(codes.cpu().numpy(), 4, d), k_ref, T_ref, c, f"h={h} identity={ident}")
     got = norms.cpu().numpy().astype(np.float64)
     if weights:
-        r_ref = oracle.bf16_rne(s_ref)
-        assert np.all(np.abs(got - r_ref) <= 2.0 ** (np.floor(np.log2(r_ref)) - 7))
+        check_rprime(got, s_ref, "r'")
     else:
         assert np.max(np.abs(got - s_ref) / s_ref) < 1e-6
 
@@ -177,8 +177,7 @@ def test_quantize_composed_passes(orbq, passes, weights, kind):
     check_codes(oracle.unpack_codes(codes.cpu().numpy(), 4, d), k_ref, T_ref, c, f"passes={passes} {kind}")
     got = norms.cpu().numpy().astype(np.float64)
     if weights:
-        r_ref = oracle.bf16_rne(s_ref)
-        assert np.all(np.abs(got - r_ref) <= 2.0 ** (np.floor(np.log2(r_ref)) - 7))
+        check_rprime(got, s_ref, "r'")
     else:
         assert np.max(np.abs(got - s_ref) / s_ref) < 1e-6
 
@@ -231,13 +230,7 @@ def _quant_case(orbq, name, rows=None, sample=None, weights=False):
     k_gpu = oracle.unpack_codes(codes[idx], bits, L.d)
     check_codes(k_gpu, k_ref, T_ref, c, f"{name} codes")
     if weights:
-        r_ref = oracle.bf16_rne(s_ref)
-        diff = norms[idx] != r_ref
-        if diff.any():
-            ulp = 2.0 ** (np.floor(np.log2(r_ref[diff])) - 7)
-            assert np.all(np.abs(norms[idx][diff] - r_ref[diff]) <= ulp)
-            mid = r_ref[diff] + np.sign(norms[idx][diff] - r_ref[diff]) * ulp / 2
-            assert np.all(np.abs(s_ref[diff] - mid) <= 1e-6 * s_ref[diff])
+        check_rprime(norms[idx], s_ref, f"{name} r'")
     else:
         assert np.max(np.abs(norms[idx] - s_ref) / s_ref) < 1e-6
     return codes, norms
@@ -268,6 +261,40 @@ def test_fold_weights_sampled(orbq, name):
     _quant_case(orbq, name, weights=True, sample=lambda n: _sample_rows(n, 40, 1))
 
 
+@pytest.mark.parametrize("d,h,bits,n,weights", [(256, 64, 3, 37, False), (1536, 128, 6, 35, False),
+                                                (3072, 128, 2, 19, True), (8960, 128, 6, 7, False),
+                                                (256, 64, 4, 70, True), (3072, 128, 3, 5, True),
+                                                (12288, 128, 4, 3, False), (1536, 128, 4, 1, True)])
+def test_quantize_outputs_every_byte_written(orbq, d, h, bits, n, weights):
+    """Code and norm buffers filled with 0xFF before the call come out byte-identical to a run
+    into zero-filled buffers: every byte of every row is written, the 3- and 6-bit row tails and
+    the ragged last token group included, and nothing past the outputs (a 0xFF guard row after
+    them stays untouched)."""
+    torch = torch_mod()
+    log(f"poisoned outputs d={d} h={h} bits={bits} n={n} weights={weights}")
+    rot = gpu_rotation(orbq, d, h)
+    cb, _ = gpu_codebook(orbq, d, bits)
+    src = workloads.weights(n, d, 700 + d) if weights else workloads.activations(n, d, 701 + d, kind="heavy")
+    dsrc = dev_bf16(src)
+    rb = orbq.codes_row_bytes(d, bits)
+    ndt = torch.bfloat16 if weights else torch.float32
+    outs = []
+    for fill in (0xFF, 0x00):
+        codes = torch.full((n + 1, rb), fill, dtype=torch.uint8, device="cuda")
+        norms = torch.empty((n + 1,), dtype=ndt, device="cuda")
+        norms.view(torch.int16 if weights else torch.int32).fill_(-1 if fill else 0)
+        f = orbq.fold_weights if weights else orbq.rpbh_quantize
+        f(dsrc, rot, cb, out_codes=codes[:n], out_norms=norms[:n])
+        torch.cuda.synchronize()
+        outs.append((codes.cpu().numpy(), norms.view(torch.uint8).cpu().numpy()))
+    (c1, n1), (c0, n0) = outs
+    assert np.array_equal(c1[:n], c0[:n]), "a code byte kept its fill value"
+    esz = 2 if weights else 4
+    assert np.array_equal(n1[:n * esz], n0[:n * esz]), "a norm byte kept its fill value"
+    assert (c1[n] == 0xFF).all() and (c0[n] == 0).all(), "codes written past the last row"
+    assert (n1[n * esz:] == 0xFF).all() and (n0[n * esz:] == 0).all(), "norms written past the last row"
+
+
 @pytest.mark.parametrize("d,h,n,weights", [(3072, 128, 333, False), (3072, 128, 97, True), (256, 64, 70, False)])
 def test_quantize_3bit(orbq, d, h, n, weights):
     """3-bit codes (W3A3): 16 codes per lane in 6 bytes (three 16-bit stores at 2-byte aligned
@@ -286,8 +313,7 @@ def test_quantize_3bit(orbq, d, h, n, weights):
     check_codes(oracle.unpack_codes(codes.cpu().numpy(), 3, d), k_ref, T_ref, c, "3-bit")
     got = norms.cpu().numpy().astype(np.float64)
     if weights:
-        r_ref = oracle.bf16_rne(s_ref)
-        assert np.all(np.abs(got - r_ref) <= 2.0 ** (np.floor(np.log2(r_ref)) - 7))
+        check_rprime(got, s_ref, "r'")
     else:
         assert np.max(np.abs(got - s_ref) / s_ref) < 1e-6
 
