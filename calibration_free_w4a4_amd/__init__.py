@@ -21,7 +21,7 @@ import numpy as np
 
 __all__ = [
     "OrbqError", "library_path", "load", "Rotation", "Codebook", "codes_row_bytes", "fold_weights",
-    "rpbh_quantize", "lut_gemm", "linear_workspace_bytes", "linear", "test_rotate", "test_quantize_t",
+    "rpbh_quantize", "lut_gemm", "linear_workspace_bytes", "linear", "linear_noalloc", "test_rotate", "test_quantize_t",
     "F32", "BF16",
 ]
 
@@ -73,6 +73,9 @@ _SIGS = {
     "orbq_linear_act": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), ctypes.POINTER(_Codebook), _F,
                                        _P, _P, ctypes.POINTER(_Codebook), _I64, _P, ctypes.c_size_t, ctypes.c_int,
                                        _P, ctypes.c_int, _I64, _P]),
+    "orbq_linear_noalloc": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), ctypes.POINTER(_Codebook), _F,
+                                           _P, _P, ctypes.POINTER(_Codebook), _I64, ctypes.c_int, _P, ctypes.c_int, _I64,
+                                           _P]),
     "orbq_rpbh_flatness": (ctypes.c_int, [_P, _I64, _I64, _I64, _P, _P, _P]),
     "orbq_linear_a16_workspace_bytes": (ctypes.c_size_t, [_I64, _I64, _I64]),
     "orbq_linear_a16": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), _P, _P, ctypes.POINTER(_Codebook),
@@ -290,6 +293,28 @@ def linear(X, rot: Rotation, cb_a: Codebook, w_codes, w_norms, cb_w: Codebook, e
                                       w_codes.data_ptr(), w_norms.data_ptr(), ctypes.byref(w), m, workspace.data_ptr(),
                                       ws_bytes, code, Y.data_ptr(), yt, Y.stride(0), _stream(torch, X.device)),
                "orbq_linear_act")
+    return Y
+
+
+NOALLOC_SCRATCH_BYTES = 16 << 20   # ORBQ_NOALLOC_SCRATCH_BYTES
+
+
+def linear_noalloc(X, rot: Rotation, cb_a: Codebook, w_codes, w_norms, cb_w: Codebook, eps: float = 1e-8,
+                   out_dtype=None, out=None, act: str = "none"):
+    """The online layer without a caller workspace (orbq_linear_noalloc): the token codes go to
+    the library's fixed per-device scratch array, so the call allocates nothing on the device
+    when `out` is given.  Calls on one GPU that overlap in time race on that array."""
+    torch = _torch()
+    _dev_tensor(X, torch.bfloat16, "linear_noalloc")
+    out_dtype = out_dtype or torch.float32
+    n, d = X.shape
+    m = w_codes.shape[0]
+    Y = out if out is not None else torch.empty((n, m), dtype=out_dtype, device=X.device)
+    r, a, w = rot.struct(), cb_a.struct(), cb_w.struct()
+    yt = BF16 if Y.dtype == torch.bfloat16 else F32
+    _check(load().orbq_linear_noalloc(X.data_ptr(), n, d, X.stride(0), ctypes.byref(r), ctypes.byref(a), eps,
+                                      w_codes.data_ptr(), w_norms.data_ptr(), ctypes.byref(w), m, _act(act),
+                                      Y.data_ptr(), yt, Y.stride(0), _stream(torch, X.device)), "orbq_linear_noalloc")
     return Y
 
 

@@ -309,6 +309,28 @@ ORBQ_API int orbq_linear_act(const void* X, int64_t n, int64_t d, int64_t ldx, c
                      ldy, stream, what);
 }
 
+ORBQ_API int orbq_linear_noalloc(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                                 const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
+                                 const orbq_codebook* cb_w, int64_t m, orbq_activation act, void* Y,
+                                 orbq_dtype y_type, int64_t ldy, void* stream) {
+  const char* what = "orbq_linear_noalloc";
+  if (!valid_act(act)) return fail(ORBQ_ERR_INVALID_ARG, "%s: unknown activation %d", what, static_cast<int>(act));
+  if (!cb_a) return fail(ORBQ_ERR_INVALID_ARG, "%s: codebook is NULL", what);
+  if (n < 0 || d <= 0) return fail(ORBQ_ERR_INVALID_ARG, "%s: bad n or d", what);
+  const size_t need = orbq_linear_workspace_bytes(n, d, cb_a->bits);
+  if (need > ORBQ_NOALLOC_SCRATCH_BYTES)
+    return fail(ORBQ_ERR_WORKSPACE, "%s: %lld x %lld at %d bits needs %zu bytes of workspace, above the %u-byte "
+                "fixed scratch (use orbq_linear_act with a caller workspace)",
+                what, (long long)n, (long long)d, cb_a->bits, need, ORBQ_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  if (n > 0 && m > 0) {
+    const int e = orbq::noalloc_scratch(&ws);
+    if (e != hipSuccess) return hip_status(e, what);
+  }
+  return linear_impl(X, n, d, ldx, rot, cb_a, eps, w_codes, w_norms, cb_w, m, ws, ORBQ_NOALLOC_SCRATCH_BYTES, act, Y,
+                     y_type, ldy, stream, what);
+}
+
 namespace {
 
 constexpr int64_t kA16Tokens = 16;  // tokens per weight-only launch

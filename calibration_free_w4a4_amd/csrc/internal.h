@@ -86,6 +86,9 @@ int launch_flatness(const uint16_t* X, int64_t n, int32_t d, int64_t ldx, float*
 int launch_quantize_t(const float* t, int64_t count, const QuantParams& qp, uint8_t* codes,
                       hipStream_t stream);
 
+// The current device's fixed workspace for orbq_linear_noalloc (noalloc.hip).
+int noalloc_scratch(void** ptr);
+
 int launch_lut_gemm(const uint8_t* x_codes, const float* x_norms, const DecodeParams& da,
                     const uint8_t* w_codes, const uint16_t* w_norms, const DecodeParams& dw,
                     int64_t n, int64_t m, int64_t d, void* Y, int y_bf16, int64_t ldy,

@@ -203,6 +203,25 @@ int orbq_linear_act(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq
                     const orbq_codebook* cb_w, int64_t m, void* workspace, size_t ws_bytes,
                     orbq_activation act, void* Y, orbq_dtype y_type, int64_t ldy, void* stream);
 
+/* orbq_linear_act for callers that cannot allocate device memory (code under HIP graph capture,
+ * serving loops, harnesses that forbid hipMalloc): the same kernels and the same outputs, bit
+ * for bit, with the workspace taken from a device array inside the library instead of an
+ * argument.  The call allocates nothing.
+ *   Limit: orbq_linear_workspace_bytes(n, d, cb_a->bits) <= ORBQ_NOALLOC_SCRATCH_BYTES (16 MiB:
+ *   the 4608 x 3072 layer needs 7.1 MB, the 9216 x 3072 one 14.2 MB); larger calls return
+ *   ORBQ_ERR_WORKSPACE without launching.
+ *   Each GPU holds one such array (16 MiB, from the library's first call on that device until
+ *   the process ends), shared by every call on that GPU: calls on one GPU that overlap in time
+ *   (on different streams, or from several host threads without ordering) race on it; calls
+ *   ordered on one stream do not.  Every byte a call reads from it was written by the same call
+ *   (rpbh_quantize writes the whole workspace before the product reads it).
+ *   Other arguments, errors and layouts as in orbq_linear_act. */
+#define ORBQ_NOALLOC_SCRATCH_BYTES (16u << 20)
+int orbq_linear_noalloc(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot,
+                        const orbq_codebook* cb_a, float eps, const uint8_t* w_codes, const void* w_norms,
+                        const orbq_codebook* cb_w, int64_t m, orbq_activation act, void* Y, orbq_dtype y_type,
+                        int64_t ldy, void* stream);
+
 /* Weight-only product with bf16 activations (W4A16 and, with 2- or 6-bit weight codes,
  * W2A16 / W6A16).  The OrbitQuant pages keep the AdaLN activations in BF16 (ai-papers.net
  * OrbitQuant article, section on AdaLN handling and compression) while the AdaLN modulation
