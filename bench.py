@@ -91,7 +91,7 @@ def main() -> int:
                     help="run only a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--rotation-ablation", action="store_true",
                     help="time rpbh_quantize under the rotation variants of the rotation ablation "
-                         "(RPBH, block RHT without permutation, RHT over 1024-wide blocks, dense Haar "
+                         "(RPBH, block RHT without permutation, RHT over the widest power-of-two blocks, dense Haar "
                          "rotation as a bf16 GEMM) on the workload's activations; prints its own line")
     ap.add_argument("--mlp", action="store_true",
                     help="time the FLUX MLP pair (up-projection, GELU, down-projection; 9216 tokens, "
@@ -319,8 +319,8 @@ def rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args) -> int:
     quantize, pack) under each rotation, back to back on the same resident input.
       rpbh          block h = L.block with the random permutation (the method)
       block_rht     block h = L.block, permutation = identity
-      rht_1024      h = 1024 (the widest power-of-two block dividing d, the whole vector when
-                    d = 1024), with and without the permutation
+      rht_<h>       h = the largest power of two dividing d (1024 at d = 3072, 4096 at d = 12288,
+                    the whole vector when d is a power of two), with and without the permutation
       rpbh_2pass, rpbh_3pass  two / three composed RPBH passes, each with its own permutation and
                     signs (composed randomized Hadamard transforms)
       haar_dense    a dense d x d orthogonal rotation applied as a bf16 GEMM (torch / hipBLASLt);
@@ -333,8 +333,8 @@ def rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args) -> int:
     dev = X.device
     x_codes = torch.empty((L.n, orbq.codes_row_bytes(L.d, L.bits_a)), dtype=torch.uint8, device=dev)
     x_norms = torch.empty((L.n,), dtype=torch.float32, device=dev)
-    wide = 1
-    while wide < 1024 and L.d % (2 * wide) == 0:
+    wide = 1  # the largest power of two dividing d (the pages' default block), up to 4096
+    while wide < 4096 and L.d % (2 * wide) == 0:
         wide *= 2
     p3, s3 = workloads.rotation_passes(L.d, 3)
     variants = [("rpbh", L.block, perm, signs, 1), ("block_rht", L.block, None, signs, 1),
@@ -378,9 +378,11 @@ def rotation_ablation(orbq, L, name, X, perm, signs, cb_a, args) -> int:
 def mlp_pair(orbq, workloads, args) -> int:
     """The FLUX MLP pair on one batch: rpbh_quantize, lut_gemm (up) -> GELU -> rpbh_quantize,
     lut_gemm (down), all bf16 between the layers.  Fused: GELU (tanh form) in the
-    up-projection's epilogue.  Unfused: the up-projection stores its raw product and torch's
-    GELU runs as a separate pass.  Each kernel is timed with HIP events over `reps` repetitions
-    of the whole pair, after the settle phase."""
+    up-projection's epilogue.  Fused, folded: in addition the down layer's permutation is folded
+    into the up layer's weight-row order, so the down quantizer runs without a permutation (its
+    codes, norms and outputs are the same bits).  Unfused: the up-projection stores its raw
+    product and torch's GELU runs as a separate pass.  Each kernel is timed with HIP events over
+    `reps` repetitions of the whole pair, after the settle phase."""
     import numpy as np
     import torch
     import torch.nn.functional as F
@@ -395,10 +397,17 @@ def mlp_pair(orbq, workloads, args) -> int:
     X_bits, Wu_bits = workloads.layer_inputs(Lu)
     X, Wu, Wd = to_dev(X_bits), to_dev(Wu_bits), to_dev(workloads.weights(Ld.m, Ld.d, Ld.w_seed))
     rot_u = orbq.Rotation.create(Lu.d, Lu.block, *workloads.rotation(Lu.d))
-    rot_d = orbq.Rotation.create(Ld.d, Ld.block, *workloads.rotation(Ld.d))
+    perm_d, signs_d = workloads.rotation(Ld.d)
+    rot_d = orbq.Rotation.create(Ld.d, Ld.block, perm_d, signs_d)
     cb_u, cb_d = orbq.Codebook.lloyd_max(Lu.d, 4), orbq.Codebook.lloyd_max(Ld.d, 4)
     wcu, wnu = orbq.fold_weights(Wu, rot_u, cb_u)
     wcd, wnd = orbq.fold_weights(Wd, rot_d, cb_d)
+    # The down layer's permutation folded into the up layer: the up layer's weight rows stored in
+    # pi_down order (row j holds original row pi_down[j], an offline re-indexing), so that its
+    # GELU output arrives already permuted and the down quantizer applies signs and blocks only
+    # (perm = NULL, same signs and block).  GELU is elementwise, so it commutes with the permutation.
+    wcu_f, wnu_f = orbq.fold_weights(Wu[torch.from_numpy(perm_d.astype(np.int64)).to(dev)].contiguous(), rot_u, cb_u)
+    rot_d_f = orbq.Rotation.create(Ld.d, Ld.block, None, signs_d)
     xcu = torch.empty((n, orbq.codes_row_bytes(Lu.d, 4)), dtype=torch.uint8, device=dev)
     xsu = torch.empty((n,), dtype=torch.float32, device=dev)
     xcd = torch.empty((n, orbq.codes_row_bytes(Ld.d, 4)), dtype=torch.uint8, device=dev)
@@ -407,29 +416,34 @@ def mlp_pair(orbq, workloads, args) -> int:
     H2 = torch.empty_like(H)
     Y = torch.empty((n, Ld.m), dtype=torch.bfloat16, device=dev)
 
-    def stages(fused: bool):
+    def stages(variant: str):
         st = [lambda: orbq.rpbh_quantize(X, rot_u, cb_u, out_codes=xcu, out_norms=xsu)]
-        if fused:
+        if variant == "fused":
             st.append(lambda: orbq.lut_gemm(xcu, xsu, cb_u, wcu, wnu, cb_u, Lu.d, out=H, act="gelu_tanh"))
+            st.append(lambda: orbq.rpbh_quantize(H, rot_d, cb_d, out_codes=xcd, out_norms=xsd))
+        elif variant == "fused_folded":
+            st.append(lambda: orbq.lut_gemm(xcu, xsu, cb_u, wcu_f, wnu_f, cb_u, Lu.d, out=H, act="gelu_tanh"))
+            st.append(lambda: orbq.rpbh_quantize(H, rot_d_f, cb_d, out_codes=xcd, out_norms=xsd))
         else:
             st.append(lambda: orbq.lut_gemm(xcu, xsu, cb_u, wcu, wnu, cb_u, Lu.d, out=H2))
             st.append(lambda: torch.ops.aten.gelu.out(H2, approximate="tanh", out=H))
-        st.append(lambda: orbq.rpbh_quantize(H, rot_d, cb_d, out_codes=xcd, out_norms=xsd))
+            st.append(lambda: orbq.rpbh_quantize(H, rot_d, cb_d, out_codes=xcd, out_norms=xsd))
         st.append(lambda: orbq.lut_gemm(xcd, xsd, cb_d, wcd, wnd, cb_d, Ld.d, out=Y))
         return st
 
-    names = {True: ["rpbh_quantize_up", "lut_gemm_up_gelu", "rpbh_quantize_down", "lut_gemm_down"],
-             False: ["rpbh_quantize_up", "lut_gemm_up", "gelu_pass", "rpbh_quantize_down", "lut_gemm_down"]}
+    names = {"fused": ["rpbh_quantize_up", "lut_gemm_up_gelu", "rpbh_quantize_down", "lut_gemm_down"],
+             "fused_folded": ["rpbh_quantize_up", "lut_gemm_up_gelu", "rpbh_quantize_down_noperm", "lut_gemm_down"],
+             "unfused": ["rpbh_quantize_up", "lut_gemm_up", "gelu_pass", "rpbh_quantize_down", "lut_gemm_down"]}
     t0 = time.perf_counter()
     while time.perf_counter() - t0 < args.settle:
         for _ in range(5):
-            for f in stages(True):
+            for f in stages("fused"):
                 f()
         torch.cuda.synchronize()
     reps = max(10, args.steps // 4)
     out = {}
-    for fused in (True, False):
-        st = stages(fused)
+    for variant in ("fused", "fused_folded", "unfused"):
+        st = stages(variant)
         for _ in range(3):
             for f in st:
                 f()
@@ -444,8 +458,8 @@ def mlp_pair(orbq, workloads, args) -> int:
         torch.cuda.synchronize()
         wall = (time.perf_counter() - w0) * 1e3 / reps
         per = {nm: round(statistics.mean(ev[k][i].elapsed_time(ev[k][i + 1]) for k in range(reps)) * 1e3, 2)
-               for i, nm in enumerate(names[fused])}
-        out["fused" if fused else "unfused"] = {"us_per_kernel": per, "ms_per_pair": round(wall, 4)}
+               for i, nm in enumerate(names[variant])}
+        out[variant] = {"us_per_kernel": per, "ms_per_pair": round(wall, 4)}
     flops = 2.0 * n * Lu.d * Lu.m + 2.0 * n * Ld.d * Ld.m
     torch.cuda.synchronize()
     # the fused up-projection equals torch's GELU of the unfused one (to bf16 rounding)
@@ -460,8 +474,9 @@ def mlp_pair(orbq, workloads, args) -> int:
                       "dtype": "bf16",
                       "config": {"workload": "flux_mlp_pair", "tokens": n, "d": Lu.d, "hidden": Lu.m,
                                  "bits_w": 4, "bits_a": 4, "block": Lu.block, "gelu": "tanh"},
-                      "fused": out["fused"], "unfused": out["unfused"],
+                      "fused": out["fused"], "fused_folded": out["fused_folded"], "unfused": out["unfused"],
                       "saving_ms": round(out["unfused"]["ms_per_pair"] - out["fused"]["ms_per_pair"], 4),
+                      "folded_saving_ms": round(out["fused"]["ms_per_pair"] - out["fused_folded"]["ms_per_pair"], 4),
                       "fused_vs_torch_gelu_max_rel_diff": round(agree, 5)}), flush=True)
     return 0
 

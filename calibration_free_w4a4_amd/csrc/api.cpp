@@ -56,11 +56,13 @@ int check_rot(const orbq_rpbh* rot, int64_t d, const char* what) {
   if (!rot) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation is NULL", what);
   if (!rot->signs) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation signs are NULL", what);
   if (rot->d != d) return fail(ORBQ_ERR_INVALID_ARG, "%s: rotation d=%d but d=%lld", what, rot->d, (long long)d);
-  if (rot->block < 64 || rot->block > 1024 || (rot->block & (rot->block - 1)))
-    return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not a power of two in [64, 1024]", what, rot->block);
+  if (rot->block < 64 || rot->block > 4096 || (rot->block & (rot->block - 1)))
+    return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not a power of two in [64, 4096]", what, rot->block);
   if (d % rot->block) return fail(ORBQ_ERR_INVALID_ARG, "%s: d=%lld not a multiple of block %d", what, (long long)d, rot->block);
   if (rot->passes < 0 || rot->passes > 3)
     return fail(ORBQ_ERR_UNSUPPORTED, "%s: %d composed passes (0..3 supported)", what, rot->passes);
+  if (rot->passes > 1 && rot->block > 1024)
+    return fail(ORBQ_ERR_UNSUPPORTED, "%s: composed passes with blocks above 1024", what);
   if ((rot->perm && !aligned(rot->perm, 16)) || !aligned(rot->signs, 16))
     return fail(ORBQ_ERR_ALIGNMENT, "%s: rotation arrays must be 16-byte aligned", what);
   return ORBQ_OK;
@@ -133,8 +135,8 @@ ORBQ_API int orbq_rpbh_validate(int32_t d, int32_t block, const int32_t* perm, c
   if (!signs) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL signs", what);
   int s;
   if ((s = check_dim(d, what))) return s;
-  if (block < 64 || block > 1024 || (block & (block - 1)))
-    return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not a power of two in [64, 1024]", what, block);
+  if (block < 64 || block > 4096 || (block & (block - 1)))
+    return fail(ORBQ_ERR_UNSUPPORTED, "%s: block %d not a power of two in [64, 4096]", what, block);
   if (d % block) return fail(ORBQ_ERR_INVALID_ARG, "%s: d not a multiple of block", what);
   std::vector<unsigned char> seen(d, 0);
   for (int j = 0; j < d; ++j) {

@@ -11,6 +11,8 @@ extern template hipError_t launch_block<128>(QuantMode, int, const QuantKernelAr
 extern template hipError_t launch_block<256>(QuantMode, int, const QuantKernelArgs&, int, size_t, hipStream_t);
 extern template hipError_t launch_block<512>(QuantMode, int, const QuantKernelArgs&, int, size_t, hipStream_t);
 extern template hipError_t launch_block<1024>(QuantMode, int, const QuantKernelArgs&, int, size_t, hipStream_t);
+extern template hipError_t launch_block<2048>(QuantMode, int, const QuantKernelArgs&, int, size_t, hipStream_t);
+extern template hipError_t launch_block<4096>(QuantMode, int, const QuantKernelArgs&, int, size_t, hipStream_t);
 }  // namespace rq
 
 using namespace rq;
@@ -111,6 +113,12 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
     a.full = (quantizes && mode != QuantMode::kDecoded && a.qp.bits <= 4 && a.passes == 1 &&
               groups >= 8 * resident) ? 1 : 0;
     if (a.full) a.jf = static_cast<int32_t>(a.qp.scale) + 2;
+    // Pipelined loop (one barrier per group, double LDS for the staged rows and partials): it pays
+    // where a barrier holds many waves and each workgroup runs several groups.  Measured on MI355X:
+    // 9216 x 12288 (12 waves, 18 groups per workgroup) 63.2 -> 60.2 us, 32760 x 8960 (9 waves, 64)
+    // 199 -> 188 us; 4608 x 3072 (3 waves, 2 to 3 groups) 11.84 -> 11.97 us and 32760 x 1536
+    // (3 waves, 8 groups) 32.95 -> 33.47 us, so those keep two barriers on one buffer.
+    a.pipe = (quantizes && mode != QuantMode::kDecoded && a.passes == 1 && waves >= 6 && groups >= 2 * resident) ? 1 : 0;
   }
   // tid / lpt = (tid * magic) >> 32, exact for tid < 1024 (magic = ceil(2^32 / lpt))
   a.div_magic = static_cast<uint32_t>(((uint64_t(1) << 32) + static_cast<uint64_t>(a.lpt) - 1) / static_cast<uint64_t>(a.lpt));
@@ -132,15 +140,16 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
   const bool rotate = mode == QuantMode::kRotateOnly || mode == QuantMode::kRotateBf16;
   a.inv_scale = rotate ? rsqrt_h : static_cast<float>(static_cast<double>(a.qp.scale) /
                                                                                  std::sqrt(static_cast<double>(rot.block)));
-  // LDS: staged rows [tg][ceil(d / 128) x 512 bytes] (two buffers), decision table, partial sums
+  // LDS: staged rows [nbuf][tg][ceil(d / 128) x 256 bytes], decision table, partial sums [nbuf][tg][part_stride]
+  const int nbuf = a.pipe ? 2 : 1;
   a.row_lds = static_cast<uint32_t>((rot.d + 127) / 128) * kGroupBytes;
-  size_t lds = static_cast<size_t>(a.tg) * a.row_lds;
+  size_t lds = nbuf * static_cast<size_t>(a.tg) * a.row_lds;
   a.tbl_off = static_cast<uint32_t>(lds);
   lds = align16(lds + sizeof(float2) * 2 * a.jf);
   a.part_off = static_cast<uint32_t>(lds);
-  lds = align16(lds + sizeof(float) * a.tg * a.part_stride);
+  lds = align16(lds + nbuf * sizeof(float) * a.tg * a.part_stride);
   a.rsqrt_h = rsqrt_h;
-  if (a.passes > 1 && a.perm) {  // fp32 rows for the gathers of the later passes
+  if ((a.passes > 1 && a.perm) || rot.block > 1024) {  // fp32 rows: later passes' gathers, cross-wave stages
     a.xf_off = static_cast<uint32_t>(lds);
     lds += sizeof(float) * a.tg * rot.d;
   }
@@ -171,7 +180,9 @@ int launch_rpbh_quantize(QuantMode mode, const uint16_t* X, int64_t n, int64_t l
       case 128: e = launch_block<128>(mode, bits, c, best_threads, lds, stream); break;
       case 256: e = launch_block<256>(mode, bits, c, best_threads, lds, stream); break;
       case 512: e = launch_block<512>(mode, bits, c, best_threads, lds, stream); break;
-      default: e = launch_block<1024>(mode, bits, c, best_threads, lds, stream); break;
+      case 1024: e = launch_block<1024>(mode, bits, c, best_threads, lds, stream); break;
+      case 2048: e = launch_block<2048>(mode, bits, c, best_threads, lds, stream); break;
+      default: e = launch_block<4096>(mode, bits, c, best_threads, lds, stream); break;
     }
   }
   return static_cast<int>(e);

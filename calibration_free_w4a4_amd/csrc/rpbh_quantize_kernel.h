@@ -78,7 +78,7 @@ struct QuantKernelArgs {
   float inv_scale;  // 2^k / sqrt(h) (quantize) or 1 / sqrt(h) (rotate only)
   uint32_t codes_bytes, norms_bytes, rot_bytes;  // buffer extents (< 2^31) for bounds-dropped stores
   uint32_t x_bytes;                              // extent of X in this launch (< 2^31)
-  uint32_t row_lds;                              // LDS bytes per staged token row (both buffers)
+  uint32_t row_lds;                              // LDS bytes per staged token row
   uint32_t tbl_off, part_off, part_stride;       // LDS byte offsets: table, partials; floats per token
   int32_t passes;                                // composed RPBH passes (1..3)
   uint32_t xf_off;                               // LDS byte offset of the fp32 rows (passes > 1)
@@ -86,6 +86,7 @@ struct QuantKernelArgs {
   int32_t host_tbl;                              // 1: htbl holds the decision table (J <= 32)
   int32_t full;                                  // 1: the full-range table (2-, 3-, 4-bit, one pass)
   int32_t jf;                                    // table half-size: buckets -jf..jf-1 (2^k + 2 when full, else J)
+  int32_t pipe;                                  // 1: software-pipelined loop, staging and partials double-buffered
   QuantParams qp;
   float2 htbl[2 * kHostTableHalf];               // buckets -J..J-1 as build_table makes them
 };
@@ -281,11 +282,15 @@ __device__ __forceinline__ uint32_t row_pos(uint32_t p) { return (p >> 7) * kGro
 // amortise filling it): the decision table covers every bucket t' can reach, so the per-coordinate
 // clamp of the bucket index goes away.
 //
+// PIPE (one pass, quantizing; chosen on the host for large workgroups that run several token
+// groups): one barrier per group instead of two, with the staged rows and the norm partials
+// double-buffered in LDS (the loop at the end of the kernel says why that is safe).
+//
 // At most 80 VGPRs (six waves per SIMD) for one pass with blocks up to 256: a workgroup of 9 or 12
 // waves (d = 8960, 12288) then places two workgroups on a compute unit; at five waves per SIMD
 // (85 VGPRs, measured: 249 against 196 us at 32760 x 8960) fewer fit.  Composed passes and the
 // 512- and 1024-wide blocks (more live values in the cross-lane stages) would spill under the cap.
-template <int H, int BITS, QuantMode MODE, bool PERM, bool MULTI, bool FULL>
+template <int H, int BITS, QuantMode MODE, bool PERM, bool MULTI, bool FULL, bool PIPE>
 __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu((MULTI || H > 256) ? 1 : 6))) void k_rpbh_quantize(QuantKernelArgs a) {
   extern __shared__ __align__(16) unsigned char smem[];
   const int d = a.d;
@@ -344,7 +349,8 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu((MULTI || 
       const float2 out_neg = make_float2(__builtin_inff(), __builtin_bit_cast(float, HALF + NB));
       for (int e = tid; e < 2 * TH; e += blockDim.x) {
         const int j = e - TH;
-        tbl_all[e] = j < -J ? out_pos : j >= J ? out_neg : ka->htbl[j + J];
+        const float2 in = ka->htbl[min(max(j, -J), J - 1) + J];  // a value select, not a pointer one
+        tbl_all[e] = j < -J ? out_pos : j >= J ? out_neg : in;
       }
 #endif
     } else {
@@ -359,7 +365,7 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu((MULTI || 
   const float2* tbl = tbl_all + TH;
   // zero the padding of the partial sums (entries nseg .. 15 of each token are never written)
   if (a.row_reduce)
-    for (int e = tid; e < a.tg * kNP; e += blockDim.x)
+    for (int e = tid; e < (PIPE ? 2 : 1) * a.tg * kNP; e += blockDim.x)
       if ((e & (kNP - 1)) >= a.nseg) part[e] = 0.0f;
 
   // ---- set-up: gather addresses x[perm[j]] (LDS byte offsets) and sign masks of this lane
@@ -420,49 +426,47 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu((MULTI || 
   const uint32_t row_bytes = static_cast<uint32_t>(d * BITS / 8);
   const int stride = static_cast<int>(gridDim.x);
 
-  // ---- one token group
-  auto step = [&](int g) {
-    const int64_t row = static_cast<int64_t>(g) * a.tg + slot;
-    const bool valid = active && row < a.n;
-
-    // ---- stage this lane's chunks; partial sum of squares (idle lanes loaded zeros)
+  // ---- one token group: stage (rows into LDS buffer sb, next group's loads issued), rotate
+  // (gather, norm partials into buffer pb, FWHT), finish (token norm, quantize, store)
+  float y[kE];
+  const uint32_t stbuf = static_cast<uint32_t>(a.tg) * a.row_lds;         // second staging buffer
+  const uint32_t pbuf = static_cast<uint32_t>(a.tg) * a.part_stride * 4u;  // second partials buffer
+  auto stage = [&](int g, uint32_t sb) {
     if (active) {
-      *reinterpret_cast<uint4*>(smem + st0) = v[0];
-      *reinterpret_cast<uint4*>(smem + st1) = v[1];
-    }
-    float ss = 0.0f;
-#pragma unroll
-    for (int c = 0; c < kCH; ++c) {
-      ss = dot2_acc(v[c].x, v[c].x, ss);
-      ss = dot2_acc(v[c].y, v[c].y, ss);
-      ss = dot2_acc(v[c].z, v[c].z, ss);
-      ss = dot2_acc(v[c].w, v[c].w, ss);
+      *reinterpret_cast<uint4*>(smem + sb + st0) = v[0];
+      *reinterpret_cast<uint4*>(smem + sb + st1) = v[1];
     }
     // prefetch the next group (the last iteration reloads its own group: no branch)
     load_group(g + stride < a.ngroups ? g + stride : g, v);
-    ss = segment_sum(ss, a.seg_lev);
-    if (pwriter) *reinterpret_cast<float*>(smem + a.part_off + pw_off) = ss;
-    __syncthreads();  // staged rows and partial sums of this group are visible
-
-    // ---- gather the 16 permuted positions as bf16 pairs, signs, FWHT stage 1 (+ widening)
-    float y[kE];
+  };
+  auto rotate = [&](uint32_t sb, uint32_t pb) {
+    // ---- gather the 16 permuted positions as bf16 pairs; partial sum of squares over them;
+    // signs, FWHT stage 1 (+ widening).  The norm is summed over the gathered (rotation-order)
+    // values, so it does not depend on the order the row is stored in: a row stored permuted and
+    // rotated without the permutation gives the same bits.
+    float ss = 0.0f;
     if constexpr (PERM) {
 #pragma unroll
       for (int i = 0; i < kE / 2; ++i) {
-        const uint32_t x2 = lds_pair(smem, gaddr[2 * i], gaddr[2 * i + 1]);
+        const uint32_t x2 = lds_pair(smem + sb, gaddr[2 * i], gaddr[2 * i + 1]);
+        ss = dot2_acc(x2, x2, ss);
         y[2 * i] = dot2_v(x2, smask[i]);
         y[2 * i + 1] = dot2_neghi(x2, smask[i]);
       }
     } else {  // identity permutation (block RHT): the lane's 16 positions are contiguous
-      const uint4 c0 = *reinterpret_cast<const uint4*>(smem + idaddr);
-      const uint4 c1 = *reinterpret_cast<const uint4*>(smem + idaddr + 16u);
+      const uint4 c0 = *reinterpret_cast<const uint4*>(smem + sb + idaddr);
+      const uint4 c1 = *reinterpret_cast<const uint4*>(smem + sb + idaddr + 16u);
       const uint32_t x2s[8] = {c0.x, c0.y, c0.z, c0.w, c1.x, c1.y, c1.z, c1.w};
 #pragma unroll
       for (int i = 0; i < kE / 2; ++i) {
+        ss = dot2_acc(x2s[i], x2s[i], ss);
         y[2 * i] = dot2_v(x2s[i], smask[i]);
         y[2 * i + 1] = dot2_neghi(x2s[i], smask[i]);
       }
     }
+    if (!active) ss = 0.0f;  // idle lanes gathered slot 0's values
+    ss = segment_sum(ss, a.seg_lev);
+    if (pwriter) *reinterpret_cast<float*>(smem + a.part_off + pb + pw_off) = ss;
     // ---- FWHT stages 2..4 in registers, then the cross-lane stages
     auto fwht_tail = [&](float (&y)[kE]) {
 #pragma unroll
@@ -502,6 +506,31 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu((MULTI || 
 #pragma unroll
         for (int e = 0; e < kE; ++e)
           y[e] = __builtin_fmaf(sgn6, __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(pa, __builtin_bit_cast(int, y[e]))), y[e]);
+      }
+      // Blocks of 2048 and 4096 span 2 and 4 waves: their last one or two stages pair lanes of
+      // different waves (block lane i xor 64, xor 128; positions j0 xor 1024, xor 2048).  Each
+      // goes through the token's fp32 row in LDS: every lane writes its 16 values, a barrier,
+      // the partner's 16 are read back, and a barrier before the row is written again.
+#pragma unroll
+      for (int k = 6; (1 << k) < LPB; ++k) {
+        float* xrow = reinterpret_cast<float*>(smem + a.xf_off) + slot * d;
+        if (active) {
+#pragma unroll
+          for (int c = 0; c < kE / 4; ++c)
+            *reinterpret_cast<float4*>(xrow + j0 + 4 * c) = make_float4(y[4 * c], y[4 * c + 1], y[4 * c + 2], y[4 * c + 3]);
+        }
+        __syncthreads();
+        const float sg = (bl >> k) & 1 ? -1.0f : 1.0f;
+        const float* prow = xrow + (j0 ^ (kE << k));
+#pragma unroll
+        for (int c = 0; c < kE / 4; ++c) {
+          const float4 pv = *reinterpret_cast<const float4*>(prow + 4 * c);
+          y[4 * c] = __builtin_fmaf(sg, pv.x, y[4 * c]);
+          y[4 * c + 1] = __builtin_fmaf(sg, pv.y, y[4 * c + 1]);
+          y[4 * c + 2] = __builtin_fmaf(sg, pv.z, y[4 * c + 2]);
+          y[4 * c + 3] = __builtin_fmaf(sg, pv.w, y[4 * c + 3]);
+        }
+        __syncthreads();
       }
     };
     fwht_tail(y);
@@ -549,10 +578,13 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu((MULTI || 
         fwht_tail(y);
       }
     }
-
+  };
+  auto finish = [&](int g, uint32_t pb) {
+    const int64_t row = static_cast<int64_t>(g) * a.tg + slot;
+    const bool valid = active && row < a.n;
     // ---- token norm: the partial sums of the token's lane segments, added in a fixed order
     float s2;
-    const float* prow = reinterpret_cast<const float*>(smem + a.part_off + pr_off);
+    const float* prow = reinterpret_cast<const float*>(smem + a.part_off + pb + pr_off);
     if (a.row_reduce) {
       s2 = row16_sum(prow[threadIdx.x & (kNP - 1)]);
     } else {
@@ -706,21 +738,51 @@ __global__ __launch_bounds__(1024) __attribute__((amdgpu_waves_per_eu((MULTI || 
     }
   };
 
-  for (int g = blockIdx.x; g < a.ngroups; g += stride) {
-    __syncthreads();  // the previous group's gathers and partial reads are done
-    step(g);
+  // Pipelined (PIPE, workgroups that run several token groups): one barrier per group.  The
+  // staged rows and the norm partials alternate between two buffers, and group g is quantized
+  // after the barrier of the next group: a wave stages group g + 1 into the buffer last gathered
+  // from by group g - 1 (before the previous barrier), and writes group g + 1's partials into
+  // the buffer group g - 1's were read from (also before it).
+  // Otherwise two barriers per group, on one buffer: staged rows visible, then partials visible
+  // (every gather of the group done before the next staging).
+  int g = blockIdx.x;
+  if constexpr (!PIPE) {
+    for (; g < a.ngroups; g += stride) {
+      stage(g, 0u);
+      __syncthreads();
+      rotate(0u, 0u);
+      __syncthreads();
+      finish(g, 0u);
+    }
+  } else if (g < a.ngroups) {
+    stage(g, 0u);
+    __syncthreads();
+    rotate(0u, 0u);
+    uint32_t sb = 0u, pb = 0u;
+    for (int gn = g + stride; gn < a.ngroups; gn += stride) {
+      const uint32_t sbn = sb ^ stbuf, pbn = pb ^ pbuf;
+      stage(gn, sbn);
+      __syncthreads();
+      finish(g, pb);
+      rotate(sbn, pbn);
+      g = gn;
+      sb = sbn;
+      pb = pbn;
+    }
+    __syncthreads();
+    finish(g, pb);
   }
 }
 
 // Balanced persistent grid: every workgroup runs the same number of token groups, and all of
 // them are resident at once (as many workgroups per CU as the kernel's occupancy allows).
-template <int H, int BITS, QuantMode MODE, bool PERM, bool MULTI, bool FULL>
+template <int H, int BITS, QuantMode MODE, bool PERM, bool MULTI, bool FULL, bool PIPE = false>
 hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
   static thread_local int cached_threads = -1, cached_occ = 1;
   static thread_local size_t cached_lds = 0;
   if (threads != cached_threads || lds != cached_lds) {
     int occ = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_rpbh_quantize<H, BITS, MODE, PERM, MULTI, FULL>, threads, lds) != hipSuccess ||
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, k_rpbh_quantize<H, BITS, MODE, PERM, MULTI, FULL, PIPE>, threads, lds) != hipSuccess ||
         occ < 1)
       occ = 1;
     cached_threads = threads;
@@ -730,8 +792,15 @@ hipError_t launch_typed(const QuantKernelArgs& a, int threads, size_t lds, hipSt
   const int max_grid = device_cus() * cached_occ;
   const int iters = (a.ngroups + max_grid - 1) / max_grid;
   const int grid = (a.ngroups + iters - 1) / iters;
-  hipLaunchKernelGGL((k_rpbh_quantize<H, BITS, MODE, PERM, MULTI, FULL>), dim3(grid), dim3(threads), lds, st, a);
+  hipLaunchKernelGGL((k_rpbh_quantize<H, BITS, MODE, PERM, MULTI, FULL, PIPE>), dim3(grid), dim3(threads), lds, st, a);
   return hipGetLastError();
+}
+
+// one pass, quantizing: the pipelined loop or the two-barrier one (chosen on the host)
+template <int H, int BITS, QuantMode MODE, bool PERM, bool FULL>
+hipError_t launch_pipe(const QuantKernelArgs& a, int threads, size_t lds, hipStream_t st) {
+  return a.pipe ? launch_typed<H, BITS, MODE, PERM, false, FULL, true>(a, threads, lds, st)
+                : launch_typed<H, BITS, MODE, PERM, false, FULL, false>(a, threads, lds, st);
 }
 
 template <int H, QuantMode MODE, bool PERM, bool MULTI>
@@ -750,15 +819,15 @@ hipError_t launch_perm(int bits, const QuantKernelArgs& a, int threads, size_t l
   } else {
     switch (bits) {
       case 2:
-        return a.full ? launch_typed<H, 2, MODE, PERM, MULTI, true>(a, threads, lds, st)
-                      : launch_typed<H, 2, MODE, PERM, MULTI, false>(a, threads, lds, st);
+        return a.full ? launch_pipe<H, 2, MODE, PERM, true>(a, threads, lds, st)
+                      : launch_pipe<H, 2, MODE, PERM, false>(a, threads, lds, st);
       case 3:
-        return a.full ? launch_typed<H, 3, MODE, PERM, MULTI, true>(a, threads, lds, st)
-                      : launch_typed<H, 3, MODE, PERM, MULTI, false>(a, threads, lds, st);
+        return a.full ? launch_pipe<H, 3, MODE, PERM, true>(a, threads, lds, st)
+                      : launch_pipe<H, 3, MODE, PERM, false>(a, threads, lds, st);
       case 4:
-        return a.full ? launch_typed<H, 4, MODE, PERM, MULTI, true>(a, threads, lds, st)
-                      : launch_typed<H, 4, MODE, PERM, MULTI, false>(a, threads, lds, st);
-      default: return launch_typed<H, 6, MODE, PERM, MULTI, false>(a, threads, lds, st);
+        return a.full ? launch_pipe<H, 4, MODE, PERM, true>(a, threads, lds, st)
+                      : launch_pipe<H, 4, MODE, PERM, false>(a, threads, lds, st);
+      default: return launch_pipe<H, 6, MODE, PERM, false>(a, threads, lds, st);
     }
   }
 }

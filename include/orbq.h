@@ -49,7 +49,8 @@
  * signs) are read, never validated, by the kernels: a perm entry outside [0, d) is
  * clamped into range (garbage in, garbage out, no out-of-bounds access).
  *
- * Supported shapes: block a power of two in [64, 1024]; d a multiple of block and at most 16384;
+ * Supported shapes: block a power of two in [64, 4096] (composed passes: at most 1024); d a multiple
+ * of block and at most 16384;
  * activation bits and weight bits each in {2, 3, 4, 6}, 3-bit codes in the product only with
  * 3-bit codes (W3A3; the OrbitQuant summary's 3-bit setting).  n or m equal to 0 is a no-op.
  * Alignment: bf16 matrices and code buffers 16-byte aligned with row pitches that
@@ -90,7 +91,7 @@ typedef enum { ORBQ_ACT_NONE = 0, ORBQ_ACT_GELU_TANH = 1, ORBQ_ACT_GELU_ERF = 2 
 /* RPBH rotation for one dimension d (OrbitQuant summary, "Randomized Permuted
  * Block-Hadamard (RPBH) Rotation"; fixed once per dimension).
  *   d      dimension, multiple of block
- *   block  Hadamard block size h, a power of two in [64, 1024] (the OrbitQuant summary's
+ *   block  Hadamard block size h, a power of two in [64, 4096] (the OrbitQuant summary's
  *          "RPBH Rotation" takes the largest power of two dividing d by default; the layers
  *          here use 128)
  *   perm   [device] int32[d], a permutation of 0..d-1: (P x)[j] = x[perm[j]]; NULL means the

@@ -63,13 +63,16 @@ def test_rpbh_validate():
     assert lib.orbq_rpbh_validate(d, 64, perm.ctypes.data, s2.ctypes.data) == -1
     assert lib.orbq_rpbh_validate(d, 32, perm.ctypes.data, signs.ctypes.data) == -2
     assert lib.orbq_rpbh_validate(192, 128, perm.ctypes.data, signs.ctypes.data) == -1
-    # Hadamard blocks: powers of two in [64, 1024]; perm NULL = identity
-    p2 = np.random.default_rng(1).permutation(2048).astype(np.int32)
-    s2 = np.ones(2048, np.int8)
-    for blk, want in ((64, 0), (256, 0), (1024, 0), (2048, -2), (96, -2), (32, -2)):
-        assert lib.orbq_rpbh_validate(2048, blk, p2.ctypes.data, s2.ctypes.data) == want, blk
-    assert lib.orbq_rpbh_validate(2048, 512, None, s2.ctypes.data) == 0
-    assert lib.orbq_rpbh_validate(2048, 512, p2.ctypes.data, None) == -1
+    # Hadamard blocks: powers of two in [64, 4096] dividing d; perm NULL = identity
+    p2 = np.random.default_rng(1).permutation(8192).astype(np.int32)
+    s2 = np.ones(8192, np.int8)
+    for blk, want in ((64, 0), (256, 0), (1024, 0), (2048, 0), (4096, 0), (8192, -2), (96, -2), (32, -2)):
+        assert lib.orbq_rpbh_validate(8192, blk, p2.ctypes.data, s2.ctypes.data) == want, blk
+    assert lib.orbq_rpbh_validate(12288, 4096, None, np.ones(12288, np.int8).ctypes.data) == 0
+    assert lib.orbq_rpbh_validate(12288, 8192, None, np.ones(12288, np.int8).ctypes.data) == -2
+    assert lib.orbq_rpbh_validate(6144, 4096, None, np.ones(6144, np.int8).ctypes.data) == -1  # 4096 does not divide d
+    assert lib.orbq_rpbh_validate(8192, 512, None, s2.ctypes.data) == 0
+    assert lib.orbq_rpbh_validate(8192, 512, p2.ctypes.data, None) == -1
 
 
 def _cb_struct(c, d, bits):
@@ -131,6 +134,10 @@ def test_argument_errors_return_before_launch(cb):
     assert q(P, 8, d, d, ctypes.byref(rot), ctypes.byref(c4), float("nan"), P, P, None) == -1  # eps
     rot32 = orbq._Rpbh(d, 32, 0x1000, 0x2000)
     assert q(P, 8, d, d, ctypes.byref(rot32), ctypes.byref(c4), 1e-8, P, P, None) == -2        # block
+    dd = 8192
+    cdd, keepdd = _cb_struct(cb(dd, 4), dd, 4)
+    rot4k2 = orbq._Rpbh(dd, 4096, 0x1000, 0x2000, 2)
+    assert q(P, 8, dd, dd, ctypes.byref(rot4k2), ctypes.byref(cdd), 1e-8, P, P, None) == -2    # passes, block 4096
     rot_mis = orbq._Rpbh(d, 64, 0x1004, 0x2000)
     assert q(P, 8, d, d, ctypes.byref(rot_mis), ctypes.byref(c4), 1e-8, P, P, None) == -3      # perm alignment
     c4d, keep = _cb_struct(cb(d, 4), 512, 4)

@@ -184,15 +184,21 @@ def test_flux_mlp_pair_chain(orbq, act):
                 _sample(Ld.m, None, 256, 26))
 
 
-@pytest.mark.parametrize("bits,weights", [(2, False), (3, False), (4, False), (4, True)])
-def test_quantize_full_range_table(orbq, bits, weights):
-    """rpbh_quantize / fold_weights where every workgroup runs many token groups (4200 rows of
-    d = 12288), the launch that fills the full-range decision table (no clamp of the bucket
-    index): sampled rows' codes and norms against the oracle, and the poisoned-output check
-    (every byte of every row written)."""
+# launch forms of rpbh_quantize on MI355X (256 CUs): 12288 (12 waves, 512 resident workgroups)
+# x 4200 rows: pipelined loop + full-range table; 8960 (9 waves, 512) x 1500 rows: pipelined,
+# clamped table (and 6-bit codes); 3072 (3 waves, 2048) x 17000 rows: full-range table, two-barrier loop
+@pytest.mark.parametrize("d,n,bits,weights", [(12288, 4200, 2, False), (12288, 4200, 3, False), (12288, 4200, 4, False),
+                                              (12288, 4200, 4, True), (8960, 1500, 4, False), (8960, 1500, 6, True),
+                                              (8960, 1500, 6, False), (3072, 17000, 4, False)])
+def test_quantize_loop_and_table_forms(orbq, d, n, bits, weights):
+    """rpbh_quantize / fold_weights in the launch forms chosen by the number of token groups per
+    workgroup: the full-range decision table (no clamp of the bucket index) and the software-
+    pipelined loop (double-buffered staging and norm partials), alone and together.  Sampled
+    rows' codes and norms against the oracle, and the poisoned-output check (every byte of every
+    row written, the same bits on a second call)."""
     torch = torch_mod()
-    d, h, n = 12288, 128, 4200
-    log(f"full-range table: d={d} n={n} bits={bits} weights={weights}")
+    h = 128
+    log(f"launch forms: d={d} n={n} bits={bits} weights={weights}")
     src = workloads.weights(n, d, 811) if weights else workloads.activations(n, d, 812 + bits, kind="heavy")
     rot = orbq.Rotation.create(d, h, *workloads.rotation(d))
     cb = orbq.Codebook.lloyd_max(d, bits)
@@ -215,3 +221,40 @@ def test_quantize_full_range_table(orbq, bits, weights):
         check_rprime(got, s_ref, "r'")
     else:
         assert np.max(np.abs(got - s_ref) / s_ref) < 1e-6
+
+
+def test_flux_mlp_pair_permutation_folded(orbq):
+    """The down layer's permutation folded into the up layer (FLUX MLP pair, 9216 tokens, GELU
+    tanh form): with the up layer's weight rows stored in pi_down order (row j = original row
+    pi_down[j]), the up layer's output arrives permuted, H_f[:, j] = H[:, pi_down[j]] bit for bit
+    (GELU is elementwise), and the down quantizer without a permutation (same signs and block)
+    gives the unfolded chain's down codes, norms and outputs bit for bit."""
+    torch = torch_mod()
+    Lu, Ld = workloads.CONFIGS["flux_mlp_up"], workloads.CONFIGS["flux_mlp_down"]
+    n = Lu.n
+    X, Wu = workloads.layer_inputs(Lu)
+    Wd = workloads.weights(Ld.m, Ld.d, Ld.w_seed)
+    perm_d, signs_d = workloads.rotation(Ld.d)
+    rot_u = orbq.Rotation.create(Lu.d, Lu.block, *workloads.rotation(Lu.d))
+    rot_d = orbq.Rotation.create(Ld.d, Ld.block, perm_d, signs_d)
+    rot_d_f = orbq.Rotation.create(Ld.d, Ld.block, None, signs_d)
+    cb_u, cb_d = orbq.Codebook.lloyd_max(Lu.d, 4), orbq.Codebook.lloyd_max(Ld.d, 4)
+    dX, dWu = dev_bf16(X), dev_bf16(Wu)
+    pd = torch.from_numpy(perm_d.astype(np.int64)).cuda()
+    wcu, wnu = orbq.fold_weights(dWu, rot_u, cb_u)
+    wcu_f, wnu_f = orbq.fold_weights(dWu[pd].contiguous(), rot_u, cb_u)
+    wcd, wnd = orbq.fold_weights(dev_bf16(Wd), rot_d, cb_d)
+    assert torch.equal(wcu_f, wcu[pd]) and torch.equal(wnu_f.view(torch.int16), wnu[pd].view(torch.int16))
+    outs = []
+    for wc, wn, rot in ((wcu, wnu, rot_d), (wcu_f, wnu_f, rot_d_f)):
+        H = orbq.linear(dX, rot_u, cb_u, wc, wn, cb_u, out_dtype=torch.bfloat16, act="gelu_tanh")
+        xc, xs = orbq.rpbh_quantize(H, rot, cb_d)
+        Y = orbq.lut_gemm(xc, xs, cb_d, wcd, wnd, cb_d, Ld.d, out_dtype=torch.bfloat16)
+        outs.append((H, xc, xs, Y))
+    torch.cuda.synchronize()
+    (H, xc, xs, Y), (Hf, xcf, xsf, Yf) = outs
+    assert torch.equal(Hf.view(torch.int16), H[:, pd].view(torch.int16)), "permuted hidden tensor differs"
+    assert torch.equal(xcf, xc), "down codes differ"
+    assert torch.equal(xsf.view(torch.int32), xs.view(torch.int32)), "down norms differ"
+    assert torch.equal(Yf.view(torch.int16), Y.view(torch.int16)), "down outputs differ"
+    log(f"  folded chain: {n} tokens, hidden, down codes, norms and outputs bit-identical")

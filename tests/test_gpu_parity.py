@@ -88,10 +88,12 @@ def test_rotation_matches_dense_matrix(orbq, d, h, n):
 
 @pytest.mark.parametrize("d,h,ident", [(3072, 256, False), (3072, 512, False), (3072, 1024, False),
                                         (1024, 1024, False), (3072, 128, True), (3072, 1024, True),
-                                        (512, 64, True)])
+                                        (512, 64, True), (8192, 2048, False), (8192, 4096, False),
+                                        (12288, 4096, False), (12288, 4096, True), (4096, 4096, True)])
 def test_rotation_large_blocks_and_identity(orbq, d, h, ident):
-    """Hadamard blocks of 256..1024 (cross-lane stages by DPP row mirrors, swizzle and lane
-    exchange) and the identity permutation (perm = NULL), against the dense matrix."""
+    """Hadamard blocks of 256..4096 (cross-lane stages by DPP row mirrors, swizzle and lane
+    exchange; the stages of 2048- and 4096-wide blocks that cross waves through LDS) and the
+    identity permutation (perm = NULL), against the dense matrix."""
     log(f"rotate d={d} h={h} identity={ident}")
     perm, signs = workloads.rotation(d)
     rot = orbq.Rotation.create(d, h, None if ident else perm, signs)
@@ -107,10 +109,13 @@ def test_rotation_large_blocks_and_identity(orbq, d, h, ident):
     assert np.max(np.abs(s - nrm) / nrm) < 1e-6
 
 
-@pytest.mark.parametrize("h,ident,weights", [(1024, False, False), (128, True, False), (512, True, True)])
-def test_quantize_large_blocks_and_identity(orbq, h, ident, weights):
-    """Codes and norms with the larger blocks and without the permutation, against the oracle."""
-    d, n = 3072, 131
+@pytest.mark.parametrize("d,h,ident,weights", [(3072, 1024, False, False), (3072, 128, True, False),
+                                                (3072, 512, True, True), (12288, 4096, False, False),
+                                                (12288, 4096, True, False), (8192, 2048, False, True)])
+def test_quantize_large_blocks_and_identity(orbq, d, h, ident, weights):
+    """Codes and norms with the larger blocks (up to 4096, the largest power of two dividing the
+    FLUX hidden width 12288) and without the permutation, against the oracle."""
+    n = 131 if d <= 3072 else 37
     perm, signs = workloads.rotation(d)
     rot = orbq.Rotation.create(d, h, None if ident else perm, signs)
     cb, c = gpu_codebook(orbq, d, 4)
