@@ -9,9 +9,10 @@ weights (workloads.py).  The weights are folded once, untimed (the offline pass)
 One step = the whole online hot path on one batch: rpbh_quantize (rotate, normalise, quantize,
 pack the activations) then lut_gemm (decode, MFMA, rescale), both through the C ABI on the
 current stream, inputs already resident in HBM.  The JSON line reports orbq_linear TFLOP/s
-(2 n m d / step time) as `value`, the rpbh_quantize GB/s beside it, the MFMA roofline of the
-dominant kernel (lut_gemm) from HIP events around its launches, and the CPU oracle timed on
-a bounded sample.
+(2 n m d / step time, K steps back to back with nothing else enqueued) as `value`; a second
+pass of K steps with HIP events between the launches gives the per-kernel durations (mean and
+p10 / p50 / p90), the rpbh_quantize GB/s and the MFMA roofline of the dominant kernel
+(lut_gemm); the CPU oracle is timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -35,15 +36,32 @@ SETTLE_S = 1.0               # untimed steady-state work before the warmup steps
 CPU_SECONDS = 10.0           # the oracle's CPU leg repeats its sample until this much time
 
 
-def _sha(path: str) -> str:
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()
+CSRC = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc")
+# every source a kernel's code or its launch shape (grid, tiles, LDS layout) depends on
+KERNEL_SOURCES = {
+    "lut_gemm": ["lut_gemm_kernel.h", "lut_gemm.hip", "lut_gemm_a2.hip", "lut_gemm_a3.hip", "lut_gemm_a4.hip",
+                 "lut_gemm_a6.hip", "lut_gemm_abf.hip", "internal.h"],
+    "rpbh_quantize": ["rpbh_quantize_kernel.h", "rpbh_quantize.hip", "rpbh_quantize_b64.hip",
+                      "rpbh_quantize_b128.hip", "rpbh_quantize_b256.hip", "rpbh_quantize_b512.hip",
+                      "rpbh_quantize_b1024.hip", "rpbh_quantize_b2048.hip", "rpbh_quantize_b4096.hip",
+                      "internal.h"],
+}
 
 
-def _traffic(kernel_src: str, name: str, workload: str):
-    """HBM bytes per launch from a committed rocprofv3 --pmc summary (profiles/, lines of
-    `key: value`), or None when the summary is missing or the kernel source changed since
-    the counters were taken."""
-    path = os.path.join(ROOT, "profiles", f"{name}_{workload}.pmc.txt")
+def source_digest(kernel: str) -> str:
+    """sha256 over the kernel's sources (KERNEL_SOURCES, in that order, each file's name and
+    bytes): the tag a committed counter or trace summary carries."""
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES[kernel]:
+        h.update(f.encode() + b"\0")
+        h.update(open(os.path.join(CSRC, f), "rb").read())
+    return h.hexdigest()
+
+
+def _summary(kernel: str, suffix: str, workload: str):
+    """The `key: value` lines of a committed profiles/ summary, or None when it is missing or
+    the kernel's sources changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}.{suffix}")
     if not os.path.exists(path):
         return None
     rec = {}
@@ -51,9 +69,27 @@ def _traffic(kernel_src: str, name: str, workload: str):
         if ":" in ln and not ln.startswith(("#", " ")):
             k, v = ln.split(":", 1)
             rec[k.strip()] = v.strip()
-    if rec.get("source_sha256") != _sha(kernel_src):
-        return None
-    return float(rec["hbm_bytes_per_launch"]) if "hbm_bytes_per_launch" in rec else None
+    return rec if rec.get("source_sha256") == source_digest(kernel) else None
+
+
+def _traffic(kernel: str, workload: str):
+    """HBM bytes per launch from the committed rocprofv3 --pmc summary, or None."""
+    rec = _summary(kernel, "pmc.txt", workload)
+    return float(rec["hbm_bytes_per_launch"]) if rec and "hbm_bytes_per_launch" in rec else None
+
+
+def _trace_us(kernel: str, workload: str):
+    """Average launch duration from the committed rocprofv3 --kernel-trace summary, or None."""
+    rec = _summary(kernel, "trace.txt", workload)
+    return float(rec["average_us"]) if rec and "average_us" in rec else None
+
+
+def _pct(xs, q: float) -> float:
+    xs = sorted(xs)
+    i = (len(xs) - 1) * q
+    lo = int(i)
+    hi = min(lo + 1, len(xs) - 1)
+    return xs[lo] + (xs[hi] - xs[lo]) * (i - lo)
 
 
 def _r(v: float, nd: int):
@@ -87,6 +123,8 @@ def main() -> int:
                          "rpbh_quantize run and the torch context); for profiler runs")
     ap.add_argument("--settle", type=float, default=SETTLE_S,
                     help="seconds of untimed steps before the warmup steps (clock settle)")
+    ap.add_argument("--source-digest", action="store_true",
+                    help="print the source digests that profiles/ summaries are tagged with, and exit")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="run only a 1 GiB device copy (counter calibration) and exit")
     ap.add_argument("--rotation-ablation", action="store_true",
@@ -109,6 +147,9 @@ def main() -> int:
               "over tokens and the multi-GPU sharding is not built.", file=sys.stderr)
         return 2
 
+    if args.source_digest:
+        print(json.dumps({k: source_digest(k) for k in KERNEL_SOURCES}))
+        return 0
     if args.copy_calibration:
         return copy_calibration()
 
@@ -168,11 +209,19 @@ def main() -> int:
         gemm()
     torch.cuda.synchronize()
 
-    # ---- timed region: K steps, HIP events on the launch stream before each kernel (a step's
-    # first event also ends the previous step's lut_gemm), one more after the last step
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
+    # ---- timed region: K steps back to back on the launch stream, nothing else enqueued
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    for k in range(args.steps):
+        quantize()
+        gemm()
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / args.steps
+
+    # ---- per-kernel durations: K more steps with HIP events on the launch stream before each
+    # kernel (a step's first event also ends the previous step's lut_gemm), one after the last
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * args.steps + 1)]
     for k in range(args.steps):
         ev[2 * k].record()
         quantize()
@@ -180,10 +229,9 @@ def main() -> int:
         gemm()
     ev[2 * args.steps].record()
     torch.cuda.synchronize()
-    t1 = time.perf_counter()
-    ms_step = (t1 - t0) * 1e3 / args.steps
-    q_ms = statistics.mean(ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps))
-    g_ms = statistics.mean(ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps))
+    q_all = [ev[2 * k].elapsed_time(ev[2 * k + 1]) for k in range(args.steps)]
+    g_all = [ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps)]
+    q_ms, g_ms = statistics.mean(q_all), statistics.mean(g_all)
 
     flops = L.flops
     q_bytes = L.n * (2 * L.d + L.d * L.bits_a // 8 + 4)
@@ -259,10 +307,13 @@ def main() -> int:
         copy_same_step_us = statistics.mean(ea.elapsed_time(eb) for ea, eb in cev) * 1e3
         del src, dst, A, B, csrc, cdst
 
-    gemm_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "lut_gemm_kernel.h")
-    quant_src = os.path.join(ROOT, "calibration_free_w4a4_amd", "csrc", "rpbh_quantize.hip")
     g_tflops = flops / (g_ms * 1e-3) / 1e12
     q_gbps = q_bytes / (q_ms * 1e-3) / 1e9
+    q_trace_us = _trace_us("rpbh_quantize", name)
+    g_trace_us = _trace_us("lut_gemm", name)
+
+    def pcts(xs):
+        return {p: round(_pct(xs, q) * 1e3, 2) for p, q in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
     line = {
         "metric": "orbq_linear TFLOP/s + rpbh_quantize GB/s, FLUX-shaped 4608x3072->12288 W4A4",
         "value": round(value, 2),
@@ -282,12 +333,19 @@ def main() -> int:
         "rpbh_quantize_cold_GBps": _r(q_bytes / (q_cold_ms * 1e-3) / 1e9, 1),
         "kernel_ms": {"rpbh_quantize": round(q_ms, 5), "lut_gemm": round(g_ms, 5),
                       "rpbh_quantize_cold": _r(q_cold_ms, 5), "orbq_linear_call": _r(linear_ms, 5)},
+        # per-launch event durations over the K timed steps
+        "kernel_us_pct": {"rpbh_quantize": pcts(q_all), "lut_gemm": pcts(g_all), "launches": args.steps},
+        # the same kernels' average durations in the committed rocprofv3 kernel trace of this
+        # workload's step (null when the kernel sources changed since): no event records between
+        # launches
+        "trace_us": {"rpbh_quantize": q_trace_us, "lut_gemm": g_trace_us,
+                     "rpbh_quantize_GBps": _r(q_bytes / (q_trace_us * 1e-6) / 1e9, 1) if q_trace_us else None},
         "roofline": {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(g_tflops / BF16_PEAK_TFLOPS, 4),
-                     "traffic": _traffic(gemm_src, "lut_gemm", name)},
+                     "traffic": _traffic("lut_gemm", name)},
         "rpbh_roofline": {"bound": "hbm", "achieved": round(q_gbps, 1), "peak": HBM_PEAK_GBPS, "unit": "GB/s",
                           "frac": round(q_gbps / HBM_PEAK_GBPS, 4),
-                          "traffic": _traffic(quant_src, "rpbh_quantize", name)},
+                          "traffic": _traffic("rpbh_quantize", name)},
         "context": {"torch_bf16_matmul_TFLOPs": _r(ref_gemm_tflops, 1),
                     "torch_copy_GBps": _r(copy_gbps, 1),
                     "copy_of_rpbh_bytes_us": _r(copy_same_us, 2),

@@ -260,14 +260,23 @@ ORBQ_API size_t orbq_linear_workspace_bytes(int64_t n, int64_t d, int32_t bits_a
 
 namespace {
 
-int linear_impl(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot, const orbq_codebook* cb_a,
-                float eps, const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w, int64_t m,
-                void* workspace, size_t ws_bytes, int act, void* Y, orbq_dtype y_type, int64_t ldy, void* stream,
-                const char* what) {
+// the layer's argument checks, workspace aside
+int linear_args(const orbq_rpbh* rot, const orbq_codebook* cb_a, const uint8_t* w_codes, const void* w_norms,
+                const orbq_codebook* cb_w, int64_t n, int64_t m, int64_t d, int64_t ldx, void* Y, orbq_dtype y_type,
+                int64_t ldy, const char* what) {
   int s = gemm_checks(nullptr, nullptr, cb_a, w_codes, w_norms, cb_w, n, m, d, Y, y_type, ldy, what, false);
   if (s) return s;
   if ((s = check_rot(rot, d, what))) return s;
   if (ldx < d) return fail(ORBQ_ERR_INVALID_ARG, "%s: ldx < d", what);
+  return ORBQ_OK;
+}
+
+int linear_impl(const void* X, int64_t n, int64_t d, int64_t ldx, const orbq_rpbh* rot, const orbq_codebook* cb_a,
+                float eps, const uint8_t* w_codes, const void* w_norms, const orbq_codebook* cb_w, int64_t m,
+                void* workspace, size_t ws_bytes, int act, void* Y, orbq_dtype y_type, int64_t ldy, void* stream,
+                const char* what) {
+  int s = linear_args(rot, cb_a, w_codes, w_norms, cb_w, n, m, d, ldx, Y, y_type, ldy, what);
+  if (s) return s;
   if (n == 0 || m == 0) return ok();
   const size_t need = orbq_linear_workspace_bytes(n, d, cb_a->bits);
   if (!workspace || ws_bytes < need)
@@ -317,8 +326,9 @@ ORBQ_API int orbq_linear_noalloc(const void* X, int64_t n, int64_t d, int64_t ld
                                  orbq_dtype y_type, int64_t ldy, void* stream) {
   const char* what = "orbq_linear_noalloc";
   if (!valid_act(act)) return fail(ORBQ_ERR_INVALID_ARG, "%s: unknown activation %d", what, static_cast<int>(act));
-  if (!cb_a) return fail(ORBQ_ERR_INVALID_ARG, "%s: codebook is NULL", what);
-  if (n < 0 || d <= 0) return fail(ORBQ_ERR_INVALID_ARG, "%s: bad n or d", what);
+  // every argument is checked before the scratch is looked up (the lookup is a device call)
+  int s = linear_args(rot, cb_a, w_codes, w_norms, cb_w, n, m, d, ldx, Y, y_type, ldy, what);
+  if (s) return s;
   const size_t need = orbq_linear_workspace_bytes(n, d, cb_a->bits);
   if (need > ORBQ_NOALLOC_SCRATCH_BYTES)
     return fail(ORBQ_ERR_WORKSPACE, "%s: %lld x %lld at %d bits needs %zu bytes of workspace, above the %u-byte "

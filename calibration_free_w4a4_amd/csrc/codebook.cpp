@@ -88,8 +88,9 @@ int lloyd_max_host(int d, int bits, double* out) {
   static const GaussLegendre gl(24);
   auto w = [a](double t) { return std::exp(a * std::log1p(-t * t)); };
   std::vector<double> c(H), T(H), m0(H), b(H + 1);
-  // start: uniform grid over (0, 2.5 sigma] (any interior start converges: f_d is log-concave)
-  for (int p = 0; p < H; ++p) c[p] = 2.5 * (p + 0.5) / H / sd;
+  // start: uniform grid over (0, min(2.5 sigma, 1)) (any interior start converges: f_d is
+  // log-concave; for d < 7, 2.5 sigma passes the support's end at 1)
+  for (int p = 0; p < H; ++p) c[p] = sd > 2.5 ? 2.5 * (p + 0.5) / H / sd : (p + 0.5) / H;
   auto apply = [&]() {
     b[0] = 0.0;
     for (int p = 0; p + 1 < H; ++p) b[p + 1] = 0.5 * (c[p] + c[p + 1]);
