@@ -238,6 +238,7 @@ def main() -> int:
     value = flops / (ms_step * 1e-3) / 1e12
 
     linear_ms = q_cold_ms = ref_gemm_tflops = copy_gbps = copy_same_us = copy_same_step_us = float("nan")
+    mfma_tflops = float("nan")
     if not args.no_extras:
         # ---- the same layer through the single orbq_linear entry point (cross-check)
         for _ in range(3):
@@ -306,6 +307,22 @@ def main() -> int:
         torch.cuda.synchronize()
         copy_same_step_us = statistics.mean(ea.elapsed_time(eb) for ea, eb in cev) * 1e3
         del src, dst, A, B, csrc, cdst
+        # the matrix cores' sustained bf16 rate on register operands with random bits, two
+        # workgroups per compute unit (orbq_test_mfma_rate): the rate a bf16 contraction on real
+        # data can be held against once the chip's power limit sets its clock
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        sink = torch.empty((2 * cus * 512,), dtype=torch.float32, device=dev)
+        orbq.test_mfma_rate(2 * cus, 400, sink)
+        torch.cuda.synchronize()
+        best = float("inf")
+        for _ in range(3):
+            e0.record()
+            mfma_flops = orbq.test_mfma_rate(2 * cus, 20000, sink)
+            e1.record()
+            torch.cuda.synchronize()
+            best = min(best, e0.elapsed_time(e1))
+        mfma_tflops = mfma_flops / (best * 1e-3) / 1e12
+        del sink
 
     g_tflops = flops / (g_ms * 1e-3) / 1e12
     q_gbps = q_bytes / (q_ms * 1e-3) / 1e9
@@ -349,7 +366,10 @@ def main() -> int:
         "context": {"torch_bf16_matmul_TFLOPs": _r(ref_gemm_tflops, 1),
                     "torch_copy_GBps": _r(copy_gbps, 1),
                     "copy_of_rpbh_bytes_us": _r(copy_same_us, 2),
-                    "copy_of_rpbh_bytes_in_step_us": _r(copy_same_step_us, 2)},
+                    "copy_of_rpbh_bytes_in_step_us": _r(copy_same_step_us, 2),
+                    "mfma_sustained_TFLOPs": _r(mfma_tflops, 1),
+                    "mfma_sustained_frac_of_peak": _r(mfma_tflops / BF16_PEAK_TFLOPS, 4),
+                    "lut_gemm_frac_of_sustained": _r(g_tflops / mfma_tflops, 4)},
     }
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(L, X_bits, W_bits, perm, signs, args.cpu_tokens, args.cpu_weights)

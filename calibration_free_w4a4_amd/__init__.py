@@ -22,6 +22,7 @@ import numpy as np
 __all__ = [
     "OrbqError", "library_path", "load", "Rotation", "Codebook", "codes_row_bytes", "fold_weights",
     "rpbh_quantize", "lut_gemm", "linear_workspace_bytes", "linear", "linear_noalloc", "test_rotate", "test_quantize_t",
+    "test_mfma_rate",
     "F32", "BF16",
 ]
 
@@ -85,6 +86,7 @@ _SIGS = {
     "orbq_last_error": (ctypes.c_char_p, []),
     "orbq_test_rotate": (ctypes.c_int, [_P, _I64, _I64, _I64, ctypes.POINTER(_Rpbh), _P, _P, _P]),
     "orbq_test_quantize_t": (ctypes.c_int, [_P, _I64, ctypes.POINTER(_Codebook), _P, _P]),
+    "orbq_test_mfma_rate": (ctypes.c_int, [_I32, _I32, _P, ctypes.POINTER(ctypes.c_double), _P]),
 }
 
 
@@ -388,3 +390,16 @@ def test_quantize_t(t, cb: Codebook):
     _check(load().orbq_test_quantize_t(t.data_ptr(), t.numel(), ctypes.byref(c), out.data_ptr(),
                                        _stream(torch, t.device)), "orbq_test_quantize_t")
     return out
+
+
+def test_mfma_rate(workgroups: int, iters: int, sink=None, device=None) -> float:
+    """Test-only: launches the matrix-core rate probe (orbq_test_mfma_rate) on the current stream
+    and returns the floating-point operations of the launch; time it with events."""
+    torch = _torch()
+    dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+    if sink is None:
+        sink = torch.empty((workgroups * 512,), dtype=torch.float32, device=dev)
+    flops = ctypes.c_double(0.0)
+    _check(load().orbq_test_mfma_rate(workgroups, iters, sink.data_ptr(), ctypes.byref(flops), _stream(torch, dev)),
+           "orbq_test_mfma_rate")
+    return flops.value

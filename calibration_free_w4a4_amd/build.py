@@ -22,7 +22,7 @@ ARCH = os.environ.get("ORBQ_OFFLOAD_ARCH", "gfx950")
 
 SOURCES = ["lut_gemm_a4.hip", "lut_gemm_a6.hip", "lut_gemm_abf.hip", "lut_gemm_a2.hip", "lut_gemm_a3.hip",
            "rpbh_quantize_b128.hip", "rpbh_quantize_b64.hip", "rpbh_quantize_b256.hip", "rpbh_quantize_b512.hip",
-           "rpbh_quantize_b1024.hip", "rpbh_quantize_b2048.hip", "rpbh_quantize_b4096.hip", "rpbh_quantize.hip", "a16_gemm.hip", "lut_gemm.hip", "flatness.hip", "noalloc.hip",
+           "rpbh_quantize_b1024.hip", "rpbh_quantize_b2048.hip", "rpbh_quantize_b4096.hip", "rpbh_quantize.hip", "a16_gemm.hip", "lut_gemm.hip", "flatness.hip", "noalloc.hip", "mfma_probe.hip",
            "api.cpp",
            "codebook.cpp"]
 

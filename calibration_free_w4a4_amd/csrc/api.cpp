@@ -472,3 +472,20 @@ ORBQ_API int orbq_test_quantize_t(const float* t, int64_t count, const orbq_code
   if ((s = quant_params(cb, &qp, what))) return s;
   return hip_status(orbq::launch_quantize_t(t, count, qp, codes, static_cast<hipStream_t>(stream)), what);
 }
+
+namespace orbq {
+// mfma_probe.hip: `workgroups` x 512 threads, `iters` (a multiple of 4) MFMA steps per
+// accumulator; sink receives workgroups * 512 floats
+int launch_mfma_probe(int workgroups, int iters, float* sink, hipStream_t stream);
+double mfma_probe_flops(int workgroups, int iters);
+}  // namespace orbq
+
+ORBQ_API int orbq_test_mfma_rate(int32_t workgroups, int32_t iters, float* sink, double* flops, void* stream) {
+  const char* what = "orbq_test_mfma_rate";
+  if (workgroups < 1 || workgroups > 65536 || iters < 4 || iters % 4 || iters > (1 << 24))
+    return fail(ORBQ_ERR_INVALID_ARG, "%s: workgroups %d or iters %d out of range", what, workgroups, iters);
+  if (!sink || !flops) return fail(ORBQ_ERR_INVALID_ARG, "%s: NULL pointer", what);
+  if (!aligned(sink, 4)) return fail(ORBQ_ERR_ALIGNMENT, "%s: misaligned sink", what);
+  *flops = orbq::mfma_probe_flops(workgroups, iters);
+  return hip_status(orbq::launch_mfma_probe(workgroups, iters, sink, static_cast<hipStream_t>(stream)), what);
+}

@@ -283,6 +283,15 @@ int orbq_test_rotate(const void* X, int64_t n, int64_t d, int64_t ldx, const orb
 int orbq_test_quantize_t(const float* t, int64_t count, const orbq_codebook* cb, uint8_t* codes,
                          void* stream);
 
+/* Sustained bf16 matrix-core rate: `workgroups` workgroups of 512 threads (two waves per SIMD,
+ * as in orbq_lut_gemm) each run `iters` v_mfma_f32_32x32x16_bf16 steps into 9 accumulators per
+ * wave, on register operands with pseudo-random bits (no memory or LDS traffic).  Time it on
+ * `stream` to get the rate the matrix cores hold under load; *flops (host) receives the
+ * floating-point operations of the call.  sink [device] receives workgroups * 512 floats
+ * (4-byte aligned).  Errors: workgroups outside [1, 65536], iters not a positive multiple of 4
+ * up to 2^24, or a NULL pointer give ORBQ_ERR_INVALID_ARG. */
+int orbq_test_mfma_rate(int32_t workgroups, int32_t iters, float* sink, double* flops, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

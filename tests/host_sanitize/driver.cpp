@@ -165,6 +165,18 @@ int main() {
                                16, nullptr),
            ORBQ_ERR_WORKSPACE, "noalloc beyond the scratch");
   }
+  {  // matrix-core probe: every rejection before a launch
+    double fl = -1.0;
+    float* sink = reinterpret_cast<float*>(Y);
+    expect(orbq_test_mfma_rate(0, 400, sink, &fl, nullptr), ORBQ_ERR_INVALID_ARG, "probe: no workgroups");
+    expect(orbq_test_mfma_rate(1 << 20, 400, sink, &fl, nullptr), ORBQ_ERR_INVALID_ARG, "probe: too many");
+    expect(orbq_test_mfma_rate(256, 6, sink, &fl, nullptr), ORBQ_ERR_INVALID_ARG, "probe: iters % 4");
+    expect(orbq_test_mfma_rate(256, -4, sink, &fl, nullptr), ORBQ_ERR_INVALID_ARG, "probe: negative iters");
+    expect(orbq_test_mfma_rate(256, 400, nullptr, &fl, nullptr), ORBQ_ERR_INVALID_ARG, "probe: NULL sink");
+    expect(orbq_test_mfma_rate(256, 400, sink, nullptr, nullptr), ORBQ_ERR_INVALID_ARG, "probe: NULL flops");
+    expect(orbq_test_mfma_rate(256, 400, reinterpret_cast<float*>(reinterpret_cast<char*>(sink) + 2), &fl, nullptr),
+           ORBQ_ERR_ALIGNMENT, "probe: misaligned sink");
+  }
   ++g_checks;
   if (std::strlen(orbq_last_error()) == 0) {
     ++g_fail;

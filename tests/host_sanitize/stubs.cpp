@@ -29,6 +29,8 @@ int launch_a16_gemm(const uint16_t*, int, int64_t, const uint8_t*, const uint16_
 }
 int launch_flatness(const uint16_t*, int64_t, int, int64_t, float*, float*, hipStream_t) { reached("launch_flatness"); }
 int noalloc_scratch(void**) { reached("noalloc_scratch"); }
+int launch_mfma_probe(int, int, float*, hipStream_t) { reached("launch_mfma_probe"); }
+double mfma_probe_flops(int, int) { return 0.0; }
 int device_cus() { return 256; }
 }  // namespace orbq
 

@@ -204,6 +204,18 @@ def test_argument_errors_return_before_launch(cb):
     # quantize_t
     assert lib.orbq_test_quantize_t(P, -1, ctypes.byref(c4), P, None) == -1
     assert lib.orbq_test_quantize_t(P, 0, ctypes.byref(c4), P, None) == 0
+    # matrix-core probe: range and pointer checks before any launch
+    fl_out = ctypes.c_double(-1.0)
+    probe = lib.orbq_test_mfma_rate
+    assert probe(0, 400, P, ctypes.byref(fl_out), None) == -1           # no workgroups
+    assert probe(65537, 400, P, ctypes.byref(fl_out), None) == -1       # too many
+    assert probe(256, 402, P, ctypes.byref(fl_out), None) == -1         # iters not a multiple of 4
+    assert probe(256, 0, P, ctypes.byref(fl_out), None) == -1
+    assert probe(256, (1 << 24) + 4, P, ctypes.byref(fl_out), None) == -1
+    assert probe(256, 400, None, ctypes.byref(fl_out), None) == -1      # NULL sink
+    assert probe(256, 400, P, None, None) == -1                         # NULL flops
+    assert probe(256, 400, P + 2, ctypes.byref(fl_out), None) == -3     # misaligned sink
+    assert fl_out.value == -1.0                                        # nothing written on error
 
 
 def test_rht_passes_rule():
