@@ -45,7 +45,114 @@ struct A16Args {
   uint32_t xr_bytes;     // nt * d * 2
   uint32_t lt_lo, lt_hi, ht_lo, ht_hi;
   uint16_t mag[32];
+  // rotation inside the product (ROT): each wave computes x' for its own K split from X, perm and
+  // signs (one RPBH pass, h = 64 or 128) into LDS, at byte offset slice_off of the dynamic LDS
+  const uint16_t* X;     // [nt][ldx] bf16
+  int64_t ldx;
+  const int32_t* perm;
+  const int8_t* signs;
+  int32_t h;
+  float inv_scale;       // 1 / sqrt(h)
+  uint32_t x_bytes;      // nt * ldx * 2 (< 2^31)
+  uint32_t slice_off;
 };
+
+// x[i] += sgn * (x[i] in the DPP partner lane), for 8 registers, one v_fmac_f32_dpp each; the
+// leading s_nop 4 covers the VALU-write -> DPP-read and EXEC-write -> DPP hazards of whatever
+// the compiler placed before the block
+#define ORBQ_A16_DPP_FMAC8(CTRL, X, S)                                                             \
+  asm("s_nop 4\n"                                                                                 \
+      "v_fmac_f32_dpp %0, %0, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %1, %1, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %2, %2, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %3, %3, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %4, %4, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %5, %5, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %6, %6, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      "v_fmac_f32_dpp %7, %7, %8 " CTRL " row_mask:0xf bank_mask:0xf\n"                            \
+      : "+v"((X)[0]), "+v"((X)[1]), "+v"((X)[2]), "+v"((X)[3]), "+v"((X)[4]), "+v"((X)[5]),       \
+        "+v"((X)[6]), "+v"((X)[7])                                                                 \
+      : "v"(S))
+
+__device__ __forceinline__ float a16_dot2(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+__device__ __forceinline__ float a16_dot2_neghi(uint32_t a, uint32_t b) {
+  float r;
+  asm("v_dot2_f32_bf16 %0, %1, %2, 0 neg_hi:[0,1,0]" : "=v"(r) : "v"(a), "v"(b));
+  return r;
+}
+
+// One wave's slice of x' = Pi x (OrbitQuant summary, "Randomized Permuted Block-Hadamard (RPBH)
+// Rotation"): positions p0 .. p0 + P - 1 of the nt tokens, written as bf16 (nearest even) to
+// xl[t][p - p0], each aligned group of 8 in the decoders' order 0,2,4,6,1,3,5,7.  A lane takes 8
+// consecutive positions 8 b .. 8 b + 7 of one Hadamard block of one token; the block's h / 8
+// lanes hold b = M i over GF(2) (b0 = i0 ^ i2, b1 = i1 ^ i2, b2 = i2 ^ i3, b3 = i3), so that the
+// butterfly partners b xor 1, 2, 4, 8 are the quad_perm [1,0,3,2], quad_perm [2,3,0,1],
+// row_half_mirror and row_mirror lanes.  The arithmetic is rpbh_quantize's, stage for stage: the
+// signs and the first stage as two v_dot2_f32_bf16 per pair, the stages on position bits 1 and 2
+// as register adds, the rest as x += sgn * partner (which leaves upper lanes negated; that sign
+// folds into the scale), then x * (sign / sqrt(h)) rounded to bf16.  So x' is bit for bit the
+// rotate pass's.
+__device__ __forceinline__ void a16_rotate_slice(const A16Args& a, int lane, int p0, int P, unsigned char* xl) {
+  const int lpb = a.h >> 3;  // lanes per block: 8 or 16
+  const int nblk = P / a.h, items = a.nt * nblk;
+  const int li = lane & (lpb - 1);
+  const int b = li ^ (((li >> 2) & 1) * 3) ^ (((li >> 3) & 1) * 4);
+  const float sc = a.inv_scale * ((__builtin_popcount(b) & 1) ? -1.0f : 1.0f);
+  const float s1 = (b & 1) ? -1.0f : 1.0f, s2 = (b & 2) ? -1.0f : 1.0f;
+  const float s3 = (b & 4) ? -1.0f : 1.0f, s4 = (b & 8) ? -1.0f : 1.0f;
+  const __amdgpu_buffer_rsrc_t xsrc = uniform_rsrc(a.X, a.x_bytes);
+  const uint32_t dm1 = static_cast<uint32_t>(a.d - 1);
+  for (int q0 = 0; q0 < items; q0 += 64 / lpb) {
+    const int bi = q0 + lane / lpb;
+    const bool valid = bi < items;
+    const int t = valid ? bi / nblk : 0;
+    const int jl = (valid ? bi - t * nblk : 0) * a.h + 8 * b;  // position within the slice
+    const int j0 = p0 + jl;                                    // position within the row
+    const int4 pa = *reinterpret_cast<const int4*>(a.perm + j0);
+    const int4 pb = *reinterpret_cast<const int4*>(a.perm + j0 + 4);
+    const uint2 sg = *reinterpret_cast<const uint2*>(a.signs + j0);
+    const int pv[8] = {pa.x, pa.y, pa.z, pa.w, pb.x, pb.y, pb.z, pb.w};
+    const uint32_t rowoff = static_cast<uint32_t>(t) * static_cast<uint32_t>(a.ldx);
+    float y[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t lo = __builtin_amdgcn_raw_buffer_load_b16(
+          xsrc, (rowoff + min(static_cast<uint32_t>(pv[2 * i]), dm1)) * 2u, 0, 0);
+      const uint32_t hi = __builtin_amdgcn_raw_buffer_load_b16(
+          xsrc, (rowoff + min(static_cast<uint32_t>(pv[2 * i + 1]), dm1)) * 2u, 0, 0);
+      const uint32_t x2 = (lo & 0xFFFFu) | (hi << 16);
+      const uint32_t sb = (i < 2 ? sg.x : sg.y) >> (16 * (i & 1));  // the signs of positions 2i, 2i + 1
+      const uint32_t smask = 0x3F803F80u | ((sb & 0x80u) << 8) | ((sb & 0x8000u) << 16);
+      y[2 * i] = a16_dot2(x2, smask);
+      y[2 * i + 1] = a16_dot2_neghi(x2, smask);
+    }
+#pragma unroll
+    for (int st = 2; st < 8; st <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (i & st) continue;
+        const float u0 = y[i], u1 = y[i + st];
+        y[i] = u0 + u1;
+        y[i + st] = u0 - u1;
+      }
+    }
+    ORBQ_A16_DPP_FMAC8("quad_perm:[1,0,3,2]", y, s1);
+    ORBQ_A16_DPP_FMAC8("quad_perm:[2,3,0,1]", y, s2);
+    ORBQ_A16_DPP_FMAC8("row_half_mirror", y, s3);
+    if (lpb == 16) ORBQ_A16_DPP_FMAC8("row_mirror", y, s4);
+    auto pair = [&](int lo, int hi) {
+      typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+      const bf16x2_t p = {static_cast<__bf16>(y[lo] * sc), static_cast<__bf16>(y[hi] * sc)};
+      return __builtin_bit_cast(uint32_t, p);
+    };
+    const uint4 w = make_uint4(pair(0, 2), pair(4, 6), pair(1, 3), pair(5, 7));
+    if (valid) *reinterpret_cast<uint4*>(xl + (static_cast<uint32_t>(t) * P + jl) * 2u) = w;
+  }
+}
 
 template <int BW>
 struct CodesA16;  // the 32 codes of one (row, super-step) lane slot and their decode
@@ -109,7 +216,7 @@ struct CodesA16<6> {
   }
 };
 
-template <int BW, bool OUT_BF16, int CB>
+template <int BW, bool OUT_BF16, int CB, bool ROT>
 __global__ __launch_bounds__(64 * kA16MaxSplits) void k_a16(A16Args a) {
   constexpr int kA16Rows = 16 * CB;  // weight rows of this workgroup
   __shared__ __align__(16) unsigned char lut[BW == 6 ? 4096 * 4 : 16];
@@ -138,18 +245,46 @@ __global__ __launch_bounds__(64 * kA16MaxSplits) void k_a16(A16Args a) {
 #pragma unroll
   for (int cb = 0; cb < CB; ++cb) acc[cb] = f32x4_t{0.0f, 0.0f, 0.0f, 0.0f};
 
+  // ROT: this wave's x' slice [nt][P] in LDS (the splits' slices follow one another)
+  const int P = kA16SS * (ss1 - ss0);
+  unsigned char* xl = reinterpret_cast<unsigned char*>(red) + a.slice_off +
+                      static_cast<uint32_t>(a.nt) * (2u * kA16SS) * static_cast<uint32_t>(ss0);
+  const uint32_t lrow = static_cast<uint32_t>(m16 < a.nt ? m16 : 0) * static_cast<uint32_t>(P) * 2u;
+  CodesA16<BW> cw[CB];
+  if constexpr (ROT) {
+    // the first super-step's codes are in flight while the wave rotates its slice
+    if (ss0 < ss1) {
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        cw[cb].load(ws, static_cast<uint32_t>((16 * cb + m16) * a.rb + (ss0 * kA16SS + 32 * g) * BW / 8));
+    }
+    a16_rotate_slice(a, lane, kA16SS * ss0, P, xl);
+    __syncthreads();
+  }
   for (int ss = ss0; ss < ss1; ++ss) {
     const int k0 = ss * kA16SS + 32 * g;
     // A: the 32 x' values of token m16 that match the lane's codes, as four MFMA operands
     bf16x8_t xv[4];
+    if constexpr (ROT) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-      xv[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
-          xs, xoff + static_cast<uint32_t>((k0 + 8 * c) * 2), 0, 0));
-    CodesA16<BW> cw[CB];
+      for (int c = 0; c < 4; ++c) {
+        const uint4 v = *reinterpret_cast<const uint4*>(xl + lrow + static_cast<uint32_t>((k0 - kA16SS * ss0 + 8 * c) * 2));
+        xv[c] = __builtin_bit_cast(bf16x8_t, m16 < a.nt ? v : make_uint4(0, 0, 0, 0));
+      }
+      if (ss > ss0) {
 #pragma unroll
-    for (int cb = 0; cb < CB; ++cb)
-      cw[cb].load(ws, static_cast<uint32_t>((16 * cb + m16) * a.rb + k0 * BW / 8));
+        for (int cb = 0; cb < CB; ++cb)
+          cw[cb].load(ws, static_cast<uint32_t>((16 * cb + m16) * a.rb + k0 * BW / 8));
+      }
+    } else {
+#pragma unroll
+      for (int c = 0; c < 4; ++c)
+        xv[c] = __builtin_bit_cast(bf16x8_t, __builtin_amdgcn_raw_buffer_load_b128(
+            xs, xoff + static_cast<uint32_t>((k0 + 8 * c) * 2), 0, 0));
+#pragma unroll
+      for (int cb = 0; cb < CB; ++cb)
+        cw[cb].load(ws, static_cast<uint32_t>((16 * cb + m16) * a.rb + k0 * BW / 8));
+    }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
       const bf16x8_t av = xv[s];
@@ -224,31 +359,37 @@ int a16_column_blocks(int64_t m, int nt, int splits) {
   return best;
 }
 
-template <int CB>
-void launch_k_a16(int bits, bool out_bf16, dim3 grid, dim3 blk, size_t red, hipStream_t st, const A16Args& a) {
+template <int CB, bool ROT>
+void launch_k_a16(int bits, bool out_bf16, dim3 grid, dim3 blk, size_t lds, hipStream_t st, const A16Args& a) {
   if (out_bf16) {
     switch (bits) {
-      case 2: hipLaunchKernelGGL((k_a16<2, true, CB>), grid, blk, red, st, a); break;
-      case 3: hipLaunchKernelGGL((k_a16<3, true, CB>), grid, blk, red, st, a); break;
-      case 4: hipLaunchKernelGGL((k_a16<4, true, CB>), grid, blk, red, st, a); break;
-      default: hipLaunchKernelGGL((k_a16<6, true, CB>), grid, blk, red, st, a); break;
+      case 2: hipLaunchKernelGGL((k_a16<2, true, CB, ROT>), grid, blk, lds, st, a); break;
+      case 3: hipLaunchKernelGGL((k_a16<3, true, CB, ROT>), grid, blk, lds, st, a); break;
+      case 4: hipLaunchKernelGGL((k_a16<4, true, CB, ROT>), grid, blk, lds, st, a); break;
+      default: hipLaunchKernelGGL((k_a16<6, true, CB, ROT>), grid, blk, lds, st, a); break;
     }
   } else {
     switch (bits) {
-      case 2: hipLaunchKernelGGL((k_a16<2, false, CB>), grid, blk, red, st, a); break;
-      case 3: hipLaunchKernelGGL((k_a16<3, false, CB>), grid, blk, red, st, a); break;
-      case 4: hipLaunchKernelGGL((k_a16<4, false, CB>), grid, blk, red, st, a); break;
-      default: hipLaunchKernelGGL((k_a16<6, false, CB>), grid, blk, red, st, a); break;
+      case 2: hipLaunchKernelGGL((k_a16<2, false, CB, ROT>), grid, blk, lds, st, a); break;
+      case 3: hipLaunchKernelGGL((k_a16<3, false, CB, ROT>), grid, blk, lds, st, a); break;
+      case 4: hipLaunchKernelGGL((k_a16<4, false, CB, ROT>), grid, blk, lds, st, a); break;
+      default: hipLaunchKernelGGL((k_a16<6, false, CB, ROT>), grid, blk, lds, st, a); break;
     }
   }
 }
 
-}  // namespace
+template <bool ROT>
+void launch_cb(int cb, int bits, bool out_bf16, dim3 grid, dim3 blk, size_t lds, hipStream_t st, const A16Args& a) {
+  switch (cb) {
+    case 2: launch_k_a16<2, ROT>(bits, out_bf16, grid, blk, lds, st, a); break;
+    case 3: launch_k_a16<3, ROT>(bits, out_bf16, grid, blk, lds, st, a); break;
+    case 4: launch_k_a16<4, ROT>(bits, out_bf16, grid, blk, lds, st, a); break;
+    default: launch_k_a16<5, ROT>(bits, out_bf16, grid, blk, lds, st, a); break;
+  }
+}
 
-int launch_a16_gemm(const uint16_t* x_rot, int nt, int64_t d, const uint8_t* w_codes, const uint16_t* w_norms,
-                    const DecodeParams& dw, int64_t m, void* Y, int y_bf16, int64_t ldy, hipStream_t stream) {
-  A16Args a{};
-  a.xr = x_rot;
+void a16_setup(A16Args& a, int nt, int64_t d, const uint8_t* w_codes, const uint16_t* w_norms, const DecodeParams& dw,
+               int64_t m, void* Y, int64_t ldy) {
   a.wc = w_codes;
   a.wn = w_norms;
   a.Y = Y;
@@ -259,18 +400,60 @@ int launch_a16_gemm(const uint16_t* x_rot, int nt, int64_t d, const uint8_t* w_c
   a.rb = static_cast<int32_t>(d * dw.bits / 8);
   a.nss = static_cast<int32_t>(d / kA16SS);
   a16_splits(d, &a.splits, &a.ss_per_split);
-  a.xr_bytes = static_cast<uint32_t>(static_cast<int64_t>(nt) * d * 2);
   tab4(dw, &a.lt_lo, &a.lt_hi, &a.ht_lo, &a.ht_hi);
   for (int i = 0; i < 32; ++i) a.mag[i] = dw.mag[i];
+}
+
+size_t round16(size_t x) { return (x + 15) & ~size_t(15); }
+
+}  // namespace
+
+int launch_a16_gemm(const uint16_t* x_rot, int nt, int64_t d, const uint8_t* w_codes, const uint16_t* w_norms,
+                    const DecodeParams& dw, int64_t m, void* Y, int y_bf16, int64_t ldy, hipStream_t stream) {
+  A16Args a{};
+  a16_setup(a, nt, d, w_codes, w_norms, dw, m, Y, ldy);
+  a.xr = x_rot;
+  a.xr_bytes = static_cast<uint32_t>(static_cast<int64_t>(nt) * d * 2);
   const int cb = a16_column_blocks(m, nt, a.splits);
   const dim3 grid(static_cast<unsigned>((m + 16 * cb - 1) / (16 * cb))), blk(64 * a.splits);
   const size_t red = static_cast<size_t>(a.splits) * nt * 16 * cb * sizeof(float);
-  switch (cb) {
-    case 2: launch_k_a16<2>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a); break;
-    case 3: launch_k_a16<3>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a); break;
-    case 4: launch_k_a16<4>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a); break;
-    default: launch_k_a16<5>(dw.bits, y_bf16 != 0, grid, blk, red, stream, a); break;
-  }
+  launch_cb<false>(cb, dw.bits, y_bf16 != 0, grid, blk, red, stream, a);
+  return static_cast<int>(hipGetLastError());
+}
+
+// The weight-only product with the rotation inside it (one launch): each workgroup's waves rotate
+// their own K splits of the nt tokens into LDS (a16_rotate_slice) and stream the codes against
+// them.  Every workgroup repeats the rotation, on its critical path, so this pays only while a
+// wave's share is small: at most 8 (token, super-step) pairs, i.e. one or two gather passes per
+// wave.  Measured against the rotation launch then the product (same outputs bit for bit):
+// 2 x 3072 -> 18432 11.1-11.3 against 12.7-13.2 us, 5 x 1536 -> 8960 (h = 64) 9.1-9.5 against
+// 11.8-12.4; with 3 passes (2 x 12288 -> 3072) 18.7 against 16.6, with 8 (16 x 3072 -> 18432)
+// 24.0 against 14.1.  For one RPBH pass with a permutation and h = 64 or 128, when X's extent
+// stays below 2^31 bytes and the x' slices (nt d bf16) fit in LDS beside the partial sums;
+// otherwise returns hipErrorNotSupported and the caller rotates in a launch of its own.
+int launch_a16_gemm_rot(const uint16_t* X, int64_t ldx, int nt, int64_t d, const int32_t* perm, const int8_t* signs,
+                        int32_t h, const uint8_t* w_codes, const uint16_t* w_norms, const DecodeParams& dw, int64_t m,
+                        void* Y, int y_bf16, int64_t ldy, hipStream_t stream) {
+  if (!perm || (h != 64 && h != 128) || d % 128 || static_cast<int64_t>(nt) * ldx * 2 >= (int64_t(1) << 31))
+    return static_cast<int>(hipErrorNotSupported);
+  A16Args a{};
+  a16_setup(a, nt, d, w_codes, w_norms, dw, m, Y, ldy);
+  if (nt * a.ss_per_split > 8) return static_cast<int>(hipErrorNotSupported);
+  const int cb = a16_column_blocks(m, nt, a.splits);
+  const size_t red = round16(static_cast<size_t>(a.splits) * nt * 16 * cb * sizeof(float));
+  const size_t slices = static_cast<size_t>(nt) * d * 2;
+  const size_t fixed = (dw.bits == 6 ? 4096 * 4 : 16) + 64;  // the kernel's static LDS
+  if (red + slices + fixed > 160 * 1024) return static_cast<int>(hipErrorNotSupported);
+  a.X = X;
+  a.ldx = ldx;
+  a.perm = perm;
+  a.signs = signs;
+  a.h = h;
+  a.inv_scale = 1.0f / __builtin_sqrtf(static_cast<float>(h));
+  a.x_bytes = static_cast<uint32_t>(static_cast<int64_t>(nt) * ldx * 2);
+  a.slice_off = static_cast<uint32_t>(red);
+  const dim3 grid(static_cast<unsigned>((m + 16 * cb - 1) / (16 * cb))), blk(64 * a.splits);
+  launch_cb<true>(cb, dw.bits, y_bf16 != 0, grid, blk, red + slices, stream, a);
   return static_cast<int>(hipGetLastError());
 }
 

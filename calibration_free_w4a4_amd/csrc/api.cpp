@@ -343,6 +343,14 @@ ORBQ_API int orbq_linear_noalloc(const void* X, int64_t n, int64_t d, int64_t ld
                      y_type, ldy, stream, what);
 }
 
+namespace orbq {
+// a16_gemm.hip: the weight-only product with the rotation inside it (one RPBH pass with a
+// permutation, h = 64 or 128); hipErrorNotSupported when that form does not apply
+int launch_a16_gemm_rot(const uint16_t* X, int64_t ldx, int nt, int64_t d, const int32_t* perm, const int8_t* signs,
+                        int32_t h, const uint8_t* w_codes, const uint16_t* w_norms, const DecodeParams& dw, int64_t m,
+                        void* Y, int y_bf16, int64_t ldy, hipStream_t stream);
+}  // namespace orbq
+
 namespace {
 
 constexpr int64_t kA16Tokens = 16;  // tokens per weight-only launch
@@ -393,11 +401,20 @@ ORBQ_API int orbq_linear_a16(const void* X, int64_t n, int64_t d, int64_t ldx, c
   const hipStream_t st = static_cast<hipStream_t>(stream);
   for (int64_t t0 = 0; t0 < n; t0 += kA16Tokens) {
     const int nt = static_cast<int>(std::min<int64_t>(kA16Tokens, n - t0));
-    int e = orbq::launch_rpbh_quantize(orbq::QuantMode::kRotateBf16, static_cast<const uint16_t*>(X) + t0 * ldx, nt,
-                                       ldx, ra, nullptr, 0.0f, nullptr, norms, reinterpret_cast<float*>(xr), st);
-    if (e == hipSuccess)
-      e = orbq::launch_a16_gemm(xr, nt, d, w_codes, static_cast<const uint16_t*>(w_norms), dw, m,
-                                static_cast<unsigned char*>(Y) + t0 * ldy * esz, y_type == ORBQ_BF16, ldy, st);
+    const uint16_t* Xc = static_cast<const uint16_t*>(X) + t0 * ldx;
+    void* Yc = static_cast<unsigned char*>(Y) + t0 * ldy * esz;
+    // one RPBH pass with a permutation and h <= 128: the product rotates its own K splits
+    int e = ra.passes == 1 ? orbq::launch_a16_gemm_rot(Xc, ldx, nt, d, ra.perm, ra.signs, ra.block, w_codes,
+                                                         static_cast<const uint16_t*>(w_norms), dw, m, Yc,
+                                                         y_type == ORBQ_BF16, ldy, st)
+                           : static_cast<int>(hipErrorNotSupported);
+    if (e == hipErrorNotSupported) {
+      e = orbq::launch_rpbh_quantize(orbq::QuantMode::kRotateBf16, Xc, nt, ldx, ra, nullptr, 0.0f, nullptr, norms,
+                                     reinterpret_cast<float*>(xr), st);
+      if (e == hipSuccess)
+        e = orbq::launch_a16_gemm(xr, nt, d, w_codes, static_cast<const uint16_t*>(w_norms), dw, m, Yc,
+                                  y_type == ORBQ_BF16, ldy, st);
+    }
     if (e != hipSuccess) return hip_status(e, what);
   }
   return ok();

@@ -30,6 +30,10 @@ int launch_a16_gemm(const uint16_t*, int, int64_t, const uint8_t*, const uint16_
 int launch_flatness(const uint16_t*, int64_t, int, int64_t, float*, float*, hipStream_t) { reached("launch_flatness"); }
 int noalloc_scratch(void**) { reached("noalloc_scratch"); }
 int launch_mfma_probe(int, int, float*, hipStream_t) { reached("launch_mfma_probe"); }
+int launch_a16_gemm_rot(const uint16_t*, int64_t, int, int64_t, const int32_t*, const int8_t*, int32_t, const uint8_t*,
+                        const uint16_t*, const DecodeParams&, int64_t, void*, int, int64_t, hipStream_t) {
+  reached("launch_a16_gemm_rot");
+}
 double mfma_probe_flops(int, int) { return 0.0; }
 int device_cus() { return 256; }
 }  // namespace orbq

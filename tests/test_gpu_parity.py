@@ -551,6 +551,27 @@ def test_linear_a16_workspace_reuse(orbq):
         assert torch.equal(Y.view(torch.int16), Y0.view(torch.int16))
 
 
+@pytest.mark.parametrize("d,h,m,bw", [(3072, 128, 1000, 4), (1536, 64, 530, 2), (3072, 128, 700, 6)])
+def test_linear_a16_rotation_inside_the_product(orbq, d, h, m, bw):
+    """Chunks of a few tokens rotate inside the product (one launch); a 16-token chunk rotates in a
+    launch of its own first.  Token rows are independent, so rows taken one or two at a time
+    (the one-launch form) equal the same rows of a 16-token call (the two-launch form) bit for
+    bit.  test_linear_a16_weight_only checks both forms against the oracle."""
+    torch = torch_mod()
+    rot = gpu_rotation(orbq, d, h)
+    cb, c = gpu_codebook(orbq, d, bw)
+    W = workloads.weights(m, d, 931 + bw)
+    wc, wn = orbq.fold_weights(dev_bf16(W), rot, cb)
+    Xb = workloads.activations(16, d, seed=932, kind="heavy")
+    X = dev_bf16(Xb)
+    log(f"linear_a16 one- and two-launch forms: d={d} h={h} m={m} bw={bw}")
+    Y16 = orbq.linear_a16(X, rot, wc, wn, cb, out_dtype=torch.bfloat16)
+    for t0, k in ((0, 1), (5, 2), (15, 1)):
+        Yk = orbq.linear_a16(X[t0:t0 + k].contiguous(), rot, wc, wn, cb, out_dtype=torch.bfloat16)
+        torch.cuda.synchronize()
+        assert torch.equal(Yk.view(torch.int16), Y16[t0:t0 + k].view(torch.int16)), (t0, k)
+
+
 # ----------------------------------------------------------------- the layer
 def test_linear_equals_quantize_then_gemm(orbq):
     torch = torch_mod()
