@@ -12,7 +12,8 @@ current stream, inputs already resident in HBM.  The JSON line reports orbq_line
 (2 n m d / step time, K steps back to back with nothing else enqueued) as `value`; a second
 pass of K steps with HIP events between the launches gives the per-kernel durations (mean and
 p10 / p50 / p90), the rpbh_quantize GB/s and the MFMA roofline of the dominant kernel
-(lut_gemm); the CPU oracle is timed on a bounded sample.
+(lut_gemm); a loop of lut_gemm alone, against the step loop, gives rpbh_quantize's event-free cost
+in the step; the CPU oracle is timed on a bounded sample.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
 """
@@ -233,6 +234,17 @@ def main() -> int:
     g_all = [ev[2 * k + 1].elapsed_time(ev[2 * k + 2]) for k in range(args.steps)]
     q_ms, g_ms = statistics.mean(q_all), statistics.mean(g_all)
 
+    # ---- rpbh_quantize's event-free cost in the step: the step loop against the same loop of
+    # lut_gemm alone (which the GPU, not the host, bounds); the difference is what K1 adds to a
+    # step, its duration and the gap it brings, with no event records between launches
+    torch.cuda.synchronize()
+    t2 = time.perf_counter()
+    for _ in range(args.steps):
+        gemm()
+    torch.cuda.synchronize()
+    g_only_ms = (time.perf_counter() - t2) * 1e3 / args.steps
+    q_marginal_ms = ms_step - g_only_ms
+
     flops = L.flops
     q_bytes = L.n * (2 * L.d + L.d * L.bits_a // 8 + 4)
     value = flops / (ms_step * 1e-3) / 1e12
@@ -357,6 +369,10 @@ def main() -> int:
         # launches
         "trace_us": {"rpbh_quantize": q_trace_us, "lut_gemm": g_trace_us,
                      "rpbh_quantize_GBps": _r(q_bytes / (q_trace_us * 1e-6) / 1e9, 1) if q_trace_us else None},
+        # K1's cost in the step without events: step time less the time of lut_gemm alone
+        "rpbh_quantize_in_step_marginal": {
+            "us": round(q_marginal_ms * 1e3, 2),
+            "GBps": _r(q_bytes / (q_marginal_ms * 1e-3) / 1e9, 1) if q_marginal_ms > 0 else None},
         "roofline": {"bound": "mfma", "achieved": round(g_tflops, 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(g_tflops / BF16_PEAK_TFLOPS, 4),
                      "traffic": _traffic("lut_gemm", name)},
