@@ -570,6 +570,12 @@ def test_linear_a16_rotation_inside_the_product(orbq, d, h, m, bw):
         Yk = orbq.linear_a16(X[t0:t0 + k].contiguous(), rot, wc, wn, cb, out_dtype=torch.bfloat16)
         torch.cuda.synchronize()
         assert torch.equal(Yk.view(torch.int16), Y16[t0:t0 + k].view(torch.int16)), (t0, k)
+    # rows with a pitch above d (ldx = d + 64) through the one-launch form
+    wide = torch.zeros((2, d + 64), dtype=torch.bfloat16, device="cuda")
+    wide[:, :d] = X[3:5]
+    Yw = orbq.linear_a16(wide[:, :d], rot, wc, wn, cb, out_dtype=torch.bfloat16)
+    torch.cuda.synchronize()
+    assert torch.equal(Yw.view(torch.int16), Y16[3:5].view(torch.int16))
 
 
 # ----------------------------------------------------------------- the layer
