@@ -82,6 +82,15 @@ int launch_lut_gemm(const uint8_t* x_codes, const float* x_norms, const DecodePa
       b.Y = static_cast<unsigned char*>(Y) + (r0 * ldy + c0) * esz;
       b.tiles_n = static_cast<int32_t>((b.n + bm - 1) / bm);
       b.tiles_m = static_cast<int32_t>((b.m + bn - 1) / bn);
+      // grouped XCD order when the column tiles split evenly over the 8 XCDs: groups of token
+      // tiles x the XCD's cw column tiles, sized to about one round of its compute units.
+      // Measured at 4608 x 3072 -> 12288: fetched bytes 195 -> 109 MB per launch (9216 tokens:
+      // 709 -> 212 MB), the time unchanged (285.3 against 285.8 us); outputs identical.
+      b.group_n = 0;
+      if (b.tiles_m % 8 == 0) {
+        const int cw = b.tiles_m / 8;
+        b.group_n = std::max(1, (cus / 8) / cw);
+      }
       const int grid = b.tiles_n * b.tiles_m;
       switch (da.bits) {
         case 2: e = launch_gemm_a2(dw.bits, cfg, y_bf16 != 0, b, grid, lds, stream); break;

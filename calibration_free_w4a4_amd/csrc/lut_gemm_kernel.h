@@ -86,6 +86,7 @@ struct GemmArgs {
   int32_t nk;  // K tiles
   int32_t tiles_n, tiles_m;
   int32_t act;  // kActNone, kActGeluTanh, kActGeluErf
+  int32_t group_n;  // token tiles per group of the XCD order (0: the plain band order)
   // 4-bit decode tables: low / high bytes of the 8 bf16 magnitudes, 4 per register
   uint32_t lt_lo_a, lt_hi_a, ht_lo_a, ht_hi_a;
   uint32_t lt_lo_w, lt_hi_w, ht_lo_w, ht_hi_w;
@@ -362,12 +363,26 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave & 3, wn = wave >> 2;
 
-  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs, so give each XCD a
-  // contiguous band of tiles (neighbouring tiles share code rows in that XCD's L2)
+  // XCD-aware order: workgroups are dealt round-robin to the 8 XCDs.  With group_n > 0 (the
+  // weight-column tiles divide by 8) XCD x owns column tiles x cw .. x cw + cw - 1 (cw =
+  // tiles_m / 8) and takes them in groups of group_n token tiles x all cw columns, about one
+  // group per round of its compute units, so that a round fetches group_n token-row blocks and
+  // its own cw weight-row blocks into that XCD's L2 and the weight rows stay there from round to
+  // round.  Otherwise each XCD takes a contiguous band of the tiles in tile order.
   const int ntiles = a.tiles_n * a.tiles_m;
-  int tile = blockIdx.x;
-  if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
-  const int tn = tile % a.tiles_n, tm = tile / a.tiles_n;
+  int tn, tm;
+  if (a.group_n > 0) {
+    const int x = blockIdx.x & 7, l = blockIdx.x >> 3, cw = a.tiles_m >> 3;
+    const int span = a.group_n * cw, q = l / span, r = l - q * span;
+    const int gn = min(a.group_n, a.tiles_n - q * a.group_n);  // the last group may be shorter
+    tn = q * a.group_n + r % gn;
+    tm = x * cw + r / gn;
+  } else {
+    int tile = blockIdx.x;
+    if ((ntiles & 7) == 0) tile = (tile & 7) * (ntiles >> 3) + (tile >> 3);
+    tn = tile % a.tiles_n;
+    tm = tile / a.tiles_n;
+  }
   const int64_t row0 = static_cast<int64_t>(tn) * BM;  // token rows
   const int64_t col0 = static_cast<int64_t>(tm) * BN;  // weight rows
 
