@@ -383,6 +383,9 @@ __global__ __launch_bounds__(kThreads) void k_lut_gemm(GemmArgs a) {
     tn = tile % a.tiles_n;
     tm = tile / a.tiles_n;
   }
+  // both orders are bijections onto the tile grid; a workgroup outside it (arguments that do not
+  // belong together) leaves before touching memory, all its threads together
+  if (tn < 0 || tm < 0 || tn >= a.tiles_n || tm >= a.tiles_m) return;
   const int64_t row0 = static_cast<int64_t>(tn) * BM;  // token rows
   const int64_t col0 = static_cast<int64_t>(tm) * BN;  // weight rows
 
