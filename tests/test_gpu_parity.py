@@ -355,6 +355,16 @@ def _gemm_case(orbq, n, m, d, ba, bw, out_bf16=False, seed=7, sample=None):
     return e
 
 
+@pytest.mark.parametrize("n,m,d,out_bf16", [(1920, 12288, 256, True), (1000, 4096, 192, False),
+                                             (4608, 12288, 128, True)])
+def test_lut_gemm_grouped_tile_order(orbq, n, m, d, out_bf16):
+    """Column-tile counts that divide by 8 take the grouped XCD order (groups of token tiles x an
+    XCD's column tiles): 8 token tiles in groups of 5 (a short last group), 4 ragged token tiles in
+    one short group with an odd K-tile count, and the headline's 12 token tiles in 3 groups of 4.
+    Every output element against the oracle."""
+    _gemm_case(orbq, n, m, d, 4, 4, out_bf16=out_bf16, seed=41)
+
+
 @pytest.mark.parametrize("ba,bw", [(4, 4), (4, 2), (6, 4), (2, 2), (6, 6), (2, 6), (3, 3)])
 def test_lut_gemm_tiny_all_bit_pairs(orbq, ba, bw):
     assert _gemm_case(orbq, 64, 256, 256, ba, bw) < 1e-5
